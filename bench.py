@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of jagged candidate-isolated attention on one MI355X; prints one JSON line.
+
+A step is one pass of the hot path over one batch with its inputs resident in HBM:
+``rr_attn_plan`` (segment IDs / bounds / length-sorted work list) then ``rr_attn_run``
+(the fused attention kernel) -- or, for the candidate-only workload,
+``rr_cand_only_plan`` + ``rr_cand_only_run``.  The default workload is the
+short-history batch (B=64, prefix 4, history log-uniform in [10, 1000], 32
+candidates per user, H=4, d=64, bf16).  Steps rotate over enough copies of the
+inputs (>= 1 GiB in total) that no step finds its data in the 256 MB Infinity Cache.
+
+metric: effective (non-pad) attention TFLOP/s = 4 * d * H * sum_b [n_b^2 + c_b (n_b + 1)]
+per step / step time; candidates/s is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+ROTATE_BYTES = 1 << 30
+METRIC = "effective non-pad attention TFLOP/s + candidates/s, jagged candidate-isolated attn"
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default: about 1 s of work)")
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--config", type=int, default=2,
+                   help="2 short-history (default), 3 lognormal, 4 candidate-only, 5 skew, "
+                        "6 skew padded (attend_padded_history=True), 7 skew padded (False)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
+    return p.parse_args()
+
+
+def make_batch(cfg):
+    import workloads as W
+    if cfg == 6:
+        return W.config5_padded(attend_padded_history=True)
+    if cfg == 7:
+        return W.config5_padded(attend_padded_history=False)
+    return W.make_config(cfg)
+
+
+def describe(cfg, b):
+    import numpy as np
+    if cfg == 4:
+        h = np.diff(b.hist_offsets)
+        return {"workload": b.name, "mode": "candidate-only", "B": b.B, "Th": b.Th, "Tc": b.Tc,
+                "H": b.H, "d": b.d, "hist_len": [int(h.min()), int(np.median(h)), int(h.max())],
+                "cand_per_user": int(b.cand_offsets[1] - b.cand_offsets[0]), "seed": b.seed}
+    return {"workload": b.name, "mode": "full-sequence", "B": b.B, "T": b.T, "H": b.H, "d": b.d,
+            "prefix": int(b.prefix[0]), "hist_len": [int(b.hist.min()), int(np.median(b.hist)),
+                                                      int(b.hist.max())],
+            "cand_per_user": int(b.cand[0]), "padded": bool(b.valid is not None),
+            "attend_padded_history": bool(b.attend_padded_history), "seed": b.seed}
+
+
+def work_counts(cfg, b):
+    """(effective FLOPs, executed FLOPs, algorithmic bytes, candidates) of one step."""
+    from jagged_candidate_isolated_amd import accounting as acc
+    es = 2 if b.dtype == "bf16" else 4
+    if cfg == 4:
+        import numpy as np
+        pairs = acc.cand_only_pairs(np.diff(b.hist_offsets), np.diff(b.cand_offsets))
+        f = acc.attention_flops(pairs, b.H, b.d)
+        return f, f, acc.cand_only_bytes(b.Th, b.Tc, b.H, b.d, es), b.Tc
+    eff, ex = acc.full_mode_counts(b.prefix, b.hist, b.cand, b.pad, b.attend_padded_history)
+    return (acc.attention_flops(eff, b.H, b.d), acc.attention_flops(ex, b.H, b.d),
+            acc.full_mode_bytes(b.T, b.H, b.d, es), int(b.cand.sum()))
+
+
+def gpu_setup(cfg, b, torch, rr):
+    """Device copies of the inputs (rotated), outputs, the workspace and the two step calls."""
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if b.dtype == "bf16" else torch.float32
+
+    def up(x, dtype=None):
+        t = torch.from_numpy(x).to(dev)
+        return t if dtype is None else t.to(dtype)
+
+    if cfg == 4:
+        base = [up(b.q_cand, dt), up(b.k_hist, dt), up(b.v_hist, dt), up(b.k_cand, dt), up(b.v_cand, dt)]
+        hoff, coff = up(b.hist_offsets), up(b.cand_offsets)
+        out_like = base[0]
+        Th, Tc, H, d = b.Th, b.Tc, b.H, b.d
+        ws = torch.empty(rr.rr_cand_only_workspace_bytes(b.B, Th, Tc, H, d), dtype=torch.uint8, device=dev)
+    else:
+        base = [up(b.q, dt), up(b.k, dt), up(b.v, dt)]
+        off, cst = up(b.offsets), up(b.cand_start)
+        valid = None if b.valid is None else up(b.valid)
+        out_like = base[0]
+        ws = torch.empty(rr.rr_attn_workspace_bytes(b.B, b.T, b.H, b.d), dtype=torch.uint8, device=dev)
+    footprint = sum(t.numel() * t.element_size() for t in base) + out_like.numel() * out_like.element_size()
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    outs = [torch.empty_like(out_like) for _ in range(copies)]
+
+    if cfg == 4:
+        def plan():
+            rr.rr_cand_only_plan(hoff, coff, Th, Tc, H, d, dt, workspace=ws)
+
+        def run(i):
+            s = sets[i % copies]
+            rr.rr_cand_only_run(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies])
+    else:
+        def plan():
+            rr.rr_attn_plan(off, cst, b.T, b.H, b.d, dt, valid=valid,
+                            attend_padded_history=b.attend_padded_history, workspace=ws)
+
+        def run(i):
+            s = sets[i % copies]
+            rr.rr_attn_run(s[0], s[1], s[2], b.B, ws, out=outs[i % copies])
+    return plan, run, copies, footprint
+
+
+def cpu_baseline(cfg, b, budget_s):
+    """The oracle, as it stands, on the host cores: whole batches (or the first users of one)
+    repeated until about ``budget_s`` of CPU time; effective TFLOP/s of what it finished."""
+    import numpy as np
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    from jagged_candidate_isolated_amd import accounting as acc
+    t0 = time.perf_counter()
+    done_flops, done_cands, reps, users = 0, 0, 0, 0
+    if cfg == 4:
+        hoff, coff = b.hist_offsets, b.cand_offsets
+        hl = np.diff(hoff)
+        cl = np.diff(coff)
+        while time.perf_counter() - t0 < budget_s and users < b.B:
+            u = users
+            sl = slice(int(coff[u]), int(coff[u + 1]))
+            A.cand_only_attention(b.q_cand[sl], b.k_hist[int(hoff[u]):int(hoff[u + 1])],
+                                  b.v_hist[int(hoff[u]):int(hoff[u + 1])], b.k_cand[sl], b.v_cand[sl],
+                                  [0, int(hl[u])], [0, int(cl[u])])
+            done_flops += acc.attention_flops(acc.cand_only_pairs([hl[u]], [cl[u]]), b.H, b.d)
+            done_cands += int(cl[u])
+            users += 1
+        sample = f"first {users} of {b.B} users, candidate-only oracle"
+    else:
+        eff_all, _ = acc.full_mode_counts(b.prefix, b.hist, b.cand, b.pad, b.attend_padded_history)
+        small = b.T <= 40000
+        while time.perf_counter() - t0 < budget_s:
+            if small:
+                A.full_attention(b.q, b.k, b.v, b.offsets, b.cand_start, b.valid, b.attend_padded_history)
+                done_flops += acc.attention_flops(eff_all, b.H, b.d)
+                done_cands += int(b.cand.sum())
+                reps += 1
+            else:
+                if users >= b.B:
+                    break
+                u = users
+                lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
+                sl = slice(lo, hi)
+                valid = None if b.valid is None else b.valid[sl]
+                A.full_attention(b.q[sl], b.k[sl], b.v[sl], [0, hi - lo], [int(b.cand_start[u]) - lo],
+                                 valid, b.attend_padded_history)
+                e, _ = acc.full_mode_counts(b.prefix[u:u + 1], b.hist[u:u + 1], b.cand[u:u + 1],
+                                            b.pad[u:u + 1], b.attend_padded_history)
+                done_flops += acc.attention_flops(e, b.H, b.d)
+                done_cands += int(b.cand[u])
+                users += 1
+        sample = (f"whole batch x{reps}" if small else f"first {users} of {b.B} users") + ", float64 oracle"
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2), "candidates_per_s": done_cands / dt}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this path shards by "
+              "user with no exchange, and no multi-GPU figure is measured here.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from jagged_candidate_isolated_amd import rr
+
+    cfg = args.config
+    b = make_batch(cfg)
+    eff_flops, exec_flops, alg_bytes, n_cands = work_counts(cfg, b)
+    plan, run, copies, footprint = gpu_setup(cfg, b, torch, rr)
+    torch.cuda.synchronize()
+
+    # size the run to about a second of GPU work unless told otherwise
+    plan(); run(0); torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(3):
+        plan(); run(i)
+    torch.cuda.synchronize()
+    est = (time.perf_counter() - t) / 3
+    steps = args.steps or int(min(5000, max(20, 1.0 / max(est, 1e-6))))
+    warmup = args.warmup if args.warmup is not None else max(5, steps // 10)
+
+    for i in range(warmup):
+        plan(); run(i)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        plan()
+        ev[i][0].record(stream)
+        run(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = float(np.mean([a.elapsed_time(c) for a, c in ev]))
+    ms_per_step = wall / steps * 1e3
+    value = eff_flops / (ms_per_step / 1e3) / 1e12
+
+    flop_per_byte = eff_flops / alg_bytes
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if b.dtype == "f32":
+        roof = {"bound": "alu", "achieved": exec_flops / (kernel_ms / 1e3) / 1e12,
+                "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    elif flop_per_byte < ridge:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (kernel_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": exec_flops / (kernel_ms / 1e3) / 1e12,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "k_attn_mfma" if b.dtype == "bf16" and b.d >= 32 else "k_attn_simple"
+    roof["kernel_ms"] = kernel_ms
+    roof["alg_bytes"] = alg_bytes
+    roof["alg_flops"] = exec_flops
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
+        "config": dict(describe(cfg, b), parallelism="none (1 GPU)"),
+        "candidates_per_s": n_cands / (ms_per_step / 1e3),
+        "effective_flops_per_step": eff_flops, "executed_flops_per_step": exec_flops,
+        "executed_tflops": exec_flops / (ms_per_step / 1e3) / 1e12,
+        "input_copies_rotated": copies, "footprint_bytes": footprint,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, b, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

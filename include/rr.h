@@ -1,0 +1,186 @@
+/*
+ * rr.h -- C ABI of librr, jagged candidate-isolated attention for MI355X (gfx950).
+ *
+ * The problem (Candidate isolation attention mask page, sections "为什么需要它",
+ * "段 ID：掩码的表达方式" and "只更新候选的末尾层"; HSTU scaling notes, section
+ * "手算 padding 的浪费与 offset"):
+ *
+ *   A batch holds B users.  Their rows are concatenated (jagged values) and user b
+ *   owns rows [offsets[b], offsets[b+1]); offsets[0] = 0 and offsets[B] = T.  A
+ *   user's rows are laid out [prefix | history | candidates]; cand_start[b] is
+ *   the absolute row of its first candidate.  Each row gets a segment ID:
+ *   1 = valid prefix/history, -1 = valid candidate, 0 = padding.  A query may
+ *   read a key of its own user when the key is segment 1 and the query is not
+ *   padding, or when both are candidates at the same row.  No row ever reads
+ *   another user's rows.  Output rows of segment 0 are 0.
+ *
+ *   Candidate-only layers: candidate queries read a frozen history K/V (the
+ *   user's prefix and history states) plus their own K/V.
+ *
+ * Attention is softmax(scale * q k^T) v per head over the admitted keys.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are token-major [rows][H][d], contiguous, in device memory.  Row r,
+ *     head h, element e sits at index (r * H + h) * d + e.
+ *   - Every pointer argument is DEVICE memory owned by the caller; the library
+ *     keeps no pointer after the call returns and allocates nothing.  Scratch
+ *     comes from the caller's `workspace` (size from the *_workspace_bytes query).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *     call returns without waiting for it.  Results are valid once the stream has
+ *     reached that point.  No call synchronises the host with the device.
+ *   - Argument errors are found on the host before anything is enqueued; the call
+ *     then returns a negative rr_status and has no effect.  A failed kernel launch
+ *     returns RR_EHIP.  B = 0 or T = 0 is a valid empty call that returns RR_OK.
+ *   - Data contract, not checked on the hot path (rr_validate_jagged checks it):
+ *     offsets non-decreasing with offsets[0] = 0 and offsets[B] = T, and
+ *     offsets[b] <= cand_start[b] <= offsets[b+1].  Kernels clamp every row index
+ *     into the user's own rows, so data that breaks the contract can give wrong
+ *     numbers but never reads another user's rows or outside [0, T).
+ *   - Supported: d in {16, 32, 64, 128}; H <= 1023; dtype RR_F32 or RR_BF16 (q, k, v
+ *     and the output share it; accumulation is fp32).  scale <= 0 selects 1/sqrt(d).
+ *   - Calls on the same stream are ordered; calls on different streams that share
+ *     a workspace race.
+ */
+#ifndef RR_H_
+#define RR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RR_OK = 0,
+  RR_EINVAL = -1,        /* NULL where not allowed, negative size, inconsistent sizes */
+  RR_EDTYPE = -2,        /* dtype not RR_F32 / RR_BF16 */
+  RR_EUNSUPPORTED = -3,  /* d not in {16, 32, 64, 128}, or sizes past the documented limits */
+  RR_EWORKSPACE = -4,    /* workspace NULL or smaller than the *_workspace_bytes query */
+  RR_EHIP = -5           /* a kernel launch failed */
+} rr_status;
+
+typedef enum { RR_F32 = 0, RR_BF16 = 1 } rr_dtype;
+
+/* Text for a status code (static storage). */
+const char* rr_status_string(int status);
+
+/* Library ABI version (increments when a signature changes). */
+int rr_abi_version(void);
+
+/*
+ * rr_segment_ids -- per-row segment IDs.
+ * Candidate isolation attention mask page, section "段 ID：掩码的表达方式":
+ *   is_candidate = row >= cand_start[b];  valid = valid_mask[row] (1 when valid == NULL);
+ *   if attend_padded_history: valid = valid || !is_candidate;
+ *   seg = valid ? (is_candidate ? -1 : 1) : 0.
+ *
+ * offsets    int32 [B+1]  device
+ * cand_start int32 [B]    device, absolute rows
+ * valid      uint8 [T]    device, nonzero = valid; NULL = every row valid
+ * seg_out    int8  [T]    device, written
+ */
+int rr_segment_ids(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                   int attend_padded_history, int32_t B, int32_t T, int8_t* seg_out,
+                   hipStream_t stream);
+
+/*
+ * rr_bounds -- per-user history and candidate intervals from segment IDs.
+ * Candidate isolation attention mask page, section "段 ID：掩码的表达方式" (the operator
+ * derives [history_lower, history_upper) and [candidate_lower, candidate_upper)).
+ * Reading: the tight hull of the user's segment-1 rows and of its segment -1 rows,
+ * as absolute rows; an empty history hull is [offsets[b], offsets[b]) and an empty
+ * candidate hull [offsets[b+1], offsets[b+1]).  Segment-0 rows inside a hull
+ * (holes) stay excluded from attention by their segment ID.
+ *
+ * seg        int8  [T]    device (from rr_segment_ids)
+ * bounds_out int32 [4][B] device, written: rows hist_lo, hist_hi, cand_lo, cand_hi
+ */
+int rr_bounds(const int32_t* offsets, const int8_t* seg, int32_t B, int32_t T, int32_t* bounds_out,
+              hipStream_t stream);
+
+/* Bytes of workspace rr_attn_fwd needs for these sizes (0 on invalid sizes). */
+size_t rr_attn_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d);
+
+/*
+ * rr_attn_fwd -- full-sequence candidate-isolated attention over a jagged batch.
+ * Candidate isolation attention mask page, sections "段 ID：掩码的表达方式" (mask rule:
+ * history_mask | candidate_self_mask) and "掩码长什么样" (the P/H/C table).
+ *
+ * q, k, v, o  [T][H][d] of `dtype`, device; o is written (segment-0 rows get 0)
+ * offsets     int32 [B+1], cand_start int32 [B] (absolute rows), device
+ * valid       uint8 [T] device or NULL; attend_padded_history as in rr_segment_ids
+ * scale       softmax scale; <= 0 selects 1/sqrt(d)
+ * workspace   device scratch of at least rr_attn_workspace_bytes(B, T, H, d) bytes
+ */
+int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+                const int32_t* cand_start, const uint8_t* valid, int attend_padded_history,
+                int32_t B, int32_t T, int32_t H, int32_t d, int dtype, float scale,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rr_attn_plan + rr_attn_run -- rr_attn_fwd in two steps.
+ * The plan depends only on the batch's lengths (offsets, cand_start, valid, flag):
+ * segment IDs and bounds per user, the compacted row lists when `valid` is given,
+ * and the length-sorted list of work items.  It is written into `workspace`.
+ * rr_attn_run then computes attention from q, k, v with the plan found in the
+ * workspace, so a stack of layers over one batch can plan once and run per layer.
+ * rr_attn_run must get the same B, T, H, d and dtype as the plan it uses; the
+ * kernels check this against the plan and leave `o` unwritten if they differ.
+ * A plan stays valid until the workspace is overwritten.
+ */
+int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                 int attend_padded_history, int32_t B, int32_t T, int32_t H, int32_t d, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T, int32_t H,
+                int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Bytes of workspace rr_cand_only_attn_fwd needs for these sizes (0 on invalid sizes). */
+size_t rr_cand_only_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d);
+
+/*
+ * rr_cand_only_attn_fwd -- attention of a candidate-only layer.
+ * Candidate isolation attention mask page, section "只更新候选的末尾层": the candidate
+ * query attends the frozen history K/V (prefix and history states) and its own K/V;
+ * the result equals the candidate rows of the full layer over [history | candidates].
+ *
+ * q_cand, k_cand, v_cand, o_cand  [Tc][H][d] device; o_cand is written
+ * k_hist, v_hist                  [Th][H][d] device (frozen)
+ * hist_offsets int32 [B+1] into k_hist/v_hist; cand_offsets int32 [B+1] into the
+ *   candidate tensors (hist_offsets[B] = Th, cand_offsets[B] = Tc), device
+ * workspace    device scratch of at least rr_cand_only_workspace_bytes(...) bytes
+ */
+int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_hist,
+                          const void* k_cand, const void* v_cand, void* o_cand,
+                          const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B,
+                          int32_t Th, int32_t Tc, int32_t H, int32_t d, int dtype, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* rr_cand_only_attn_fwd in two steps, as rr_attn_plan / rr_attn_run (the frozen
+ * history K/V of a user can be planned once and reused across candidate batches of
+ * the same lengths). */
+int rr_cand_only_plan(const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B, int32_t Th,
+                      int32_t Tc, int32_t H, int32_t d, int dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+int rr_cand_only_run(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                     const void* v_cand, void* o_cand, int32_t B, int32_t Th, int32_t Tc, int32_t H,
+                     int32_t d, int dtype, float scale, const void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rr_validate_jagged -- debug check of the data contract (HSTU scaling notes, section
+ * "手算 padding 的浪费与 offset": empty sequences, offset type and user boundaries need
+ * checking).  ORs bits into *err_flags (device int32, caller zeroes it first):
+ *   1 offsets[0] != 0, 2 offsets decrease somewhere, 4 offsets[B] != T,
+ *   8 some cand_start outside [offsets[b], offsets[b+1]].
+ */
+int rr_validate_jagged(const int32_t* offsets, const int32_t* cand_start, int32_t B, int32_t T,
+                       int32_t* err_flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H_ */

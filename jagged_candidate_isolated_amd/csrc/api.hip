@@ -1,0 +1,229 @@
+// C ABI of librr: argument checks on the host, then stream-ordered launches.
+// Nothing here waits for the device or allocates memory.
+#include <math.h>
+
+#include "rr_internal.h"
+
+using namespace rr;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+int status_of(hipError_t e) { return e == hipSuccess ? RR_OK : RR_EHIP; }
+
+// The MFMA kernel takes bf16 with d >= 32; everything else runs on the VALU kernel.
+bool use_mfma(int dtype, int d) { return dtype == RR_BF16 && d >= 32; }
+int tile_rows(int dtype, int d) { return use_mfma(dtype, d) ? kBmMfma : kBmSimple; }
+
+float softmax_scale_log2(float scale, int d) {
+  const float s = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf(static_cast<float>(d));
+  return s * 1.4426950408889634f;  // log2(e)
+}
+
+// Sizes shared by both attention modes; returns RR_OK or the error.
+int check_sizes(int32_t B, int32_t rows_kv, int32_t rows_q, int32_t H, int32_t d, int dtype) {
+  if (B < 0 || rows_kv < 0 || rows_q < 0 || H < 0 || d < 0) return RR_EINVAL;
+  if (dtype != RR_F32 && dtype != RR_BF16) return RR_EDTYPE;
+  if (!supported_d(d)) return RR_EUNSUPPORTED;
+  if (H > kMaxHeads) return RR_EUNSUPPORTED;
+  if (item_upper_bound(B, rows_q, H) > 0x7fffffff) return RR_EUNSUPPORTED;
+  return RR_OK;
+}
+
+template <typename T>
+T* carve(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+struct Ws {
+  PlanHeader* header;
+  UserMeta* meta;
+  int32_t* start;
+  int32_t* idx;
+  int2* items;
+};
+
+Ws carve_all(void* ws, const WsLayout& w) {
+  return Ws{carve<PlanHeader>(ws, w.header), carve<UserMeta>(ws, w.meta), carve<int32_t>(ws, w.start),
+            carve<int32_t>(ws, w.idx), carve<int2>(ws, w.items)};
+}
+
+int run_attention(const AttnArgs& a, int dtype, int d, int bm, int64_t rows, hipStream_t stream) {
+  const int64_t grid = attn_grid(a.B, rows, a.H, bm);
+  const hipError_t e = use_mfma(dtype, d) ? launch_attn_mfma(a, d, grid, stream)
+                                          : launch_attn_simple(a, d, dtype, grid, stream);
+  return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rr_status_string(int status) {
+  switch (status) {
+    case RR_OK: return "ok";
+    case RR_EINVAL: return "invalid argument (NULL pointer, negative or inconsistent size)";
+    case RR_EDTYPE: return "unsupported dtype (use RR_F32 or RR_BF16)";
+    case RR_EUNSUPPORTED: return "unsupported size (d must be 16, 32, 64 or 128; H <= 1023)";
+    case RR_EWORKSPACE: return "workspace missing or too small";
+    case RR_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int rr_abi_version(void) { return kAbiVersion; }
+
+int rr_segment_ids(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                   int attend_padded_history, int32_t B, int32_t T, int8_t* seg_out,
+                   hipStream_t stream) {
+  if (B < 0 || T < 0) return RR_EINVAL;
+  if (B == 0 || T == 0) return RR_OK;
+  if (!offsets || !cand_start || !seg_out) return RR_EINVAL;
+  return status_of(launch_segment_ids(offsets, cand_start, valid, attend_padded_history ? 1 : 0, B,
+                                      T, seg_out, stream));
+}
+
+int rr_bounds(const int32_t* offsets, const int8_t* seg, int32_t B, int32_t T, int32_t* bounds_out,
+              hipStream_t stream) {
+  if (B < 0 || T < 0) return RR_EINVAL;
+  if (B == 0) return RR_OK;
+  if (!offsets || !bounds_out || (T > 0 && !seg)) return RR_EINVAL;
+  return status_of(launch_bounds(offsets, seg, B, T, bounds_out, stream));
+}
+
+size_t rr_attn_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d) {
+  if (check_sizes(B, T, T, H, d, RR_BF16) != RR_OK) return 0;
+  return ws_layout(B, T, T, H).total;
+}
+
+int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                 int attend_padded_history, int32_t B, int32_t T, int32_t H, int32_t d, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!offsets || !cand_start) return RR_EINVAL;
+  const WsLayout w = ws_layout(B, T, T, H);
+  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
+  const Ws p = carve_all(workspace, w);
+  const int bm = tile_rows(dtype, d);
+  const int64_t cap = attn_grid(B, T, H, bm);   // <= w.item_bound
+  hipError_t e = hipSuccess;
+  if (valid) {
+    // a padding mask: list each user's valid rows (keys first, then candidates) and its padding
+    e = launch_compact(offsets, cand_start, valid, attend_padded_history ? 1 : 0, B, T, p.meta, p.idx,
+                       stream);
+    if (e == hipSuccess)
+      e = launch_worklist(0, offsets, cand_start, 1, B, H, bm, T, T, static_cast<int>(cap), p.meta,
+                          p.start, p.items, p.header, stream);
+  } else {
+    // every row valid: segment IDs and bounds follow from offsets and cand_start directly
+    e = launch_worklist(0, offsets, cand_start, 0, B, H, bm, T, T, static_cast<int>(cap), p.meta,
+                        p.start, p.items, p.header, stream);
+  }
+  return status_of(e);
+}
+
+int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T, int32_t H,
+                int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!q || !k || !v || !o) return RR_EINVAL;
+  const WsLayout w = ws_layout(B, T, T, H);
+  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
+  const Ws p = carve_all(const_cast<void*>(workspace), w);
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.k_self = k; a.v_self = v; a.o = o;
+  a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
+  a.B = B; a.H = H; a.mode = 0; a.rows = T;
+  a.scale_log2 = softmax_scale_log2(scale, d);
+  return run_attention(a, dtype, d, tile_rows(dtype, d), T, stream);
+}
+
+int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+                const int32_t* cand_start, const uint8_t* valid, int attend_padded_history,
+                int32_t B, int32_t T, int32_t H, int32_t d, int dtype, float scale,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!q || !k || !v || !o) return RR_EINVAL;
+  const int r = rr_attn_plan(offsets, cand_start, valid, attend_padded_history, B, T, H, d, dtype,
+                             workspace, workspace_bytes, stream);
+  if (r != RR_OK) return r;
+  return rr_attn_run(q, k, v, o, B, T, H, d, dtype, scale, workspace, workspace_bytes, stream);
+}
+
+size_t rr_cand_only_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d) {
+  if (check_sizes(B, Th, Tc, H, d, RR_BF16) != RR_OK) return 0;
+  return ws_layout(B, 0, Tc, H).total;
+}
+
+int rr_cand_only_plan(const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B, int32_t Th,
+                      int32_t Tc, int32_t H, int32_t d, int dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, Th, Tc, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || Tc == 0 || H == 0) return RR_OK;
+  if (!hist_offsets || !cand_offsets) return RR_EINVAL;
+  const WsLayout w = ws_layout(B, 0, Tc, H);
+  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
+  const Ws p = carve_all(workspace, w);
+  const int bm = tile_rows(dtype, d);
+  const int64_t cap = attn_grid(B, Tc, H, bm);   // <= w.item_bound
+  return status_of(launch_worklist(1, hist_offsets, cand_offsets, 0, B, H, bm, Tc, Th,
+                                   static_cast<int>(cap), p.meta, p.start, p.items, p.header, stream));
+}
+
+int rr_cand_only_run(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                     const void* v_cand, void* o_cand, int32_t B, int32_t Th, int32_t Tc, int32_t H,
+                     int32_t d, int dtype, float scale, const void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, Th, Tc, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || Tc == 0 || H == 0) return RR_OK;
+  if (!q_cand || !k_cand || !v_cand || !o_cand) return RR_EINVAL;
+  if (Th > 0 && (!k_hist || !v_hist)) return RR_EINVAL;
+  const WsLayout w = ws_layout(B, 0, Tc, H);
+  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
+  const Ws p = carve_all(const_cast<void*>(workspace), w);
+  AttnArgs a{};
+  a.q = q_cand;
+  a.k = Th > 0 ? k_hist : k_cand;   // with no frozen rows the key list is empty for every user
+  a.v = Th > 0 ? v_hist : v_cand;
+  a.k_self = k_cand; a.v_self = v_cand; a.o = o_cand;
+  a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
+  a.B = B; a.H = H; a.mode = 1; a.rows = Tc;
+  a.scale_log2 = softmax_scale_log2(scale, d);
+  return run_attention(a, dtype, d, tile_rows(dtype, d), Tc, stream);
+}
+
+int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_hist,
+                          const void* k_cand, const void* v_cand, void* o_cand,
+                          const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B,
+                          int32_t Th, int32_t Tc, int32_t H, int32_t d, int dtype, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, Th, Tc, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || Tc == 0 || H == 0) return RR_OK;
+  if (!q_cand || !k_cand || !v_cand || !o_cand) return RR_EINVAL;
+  if (Th > 0 && (!k_hist || !v_hist)) return RR_EINVAL;
+  const int r = rr_cand_only_plan(hist_offsets, cand_offsets, B, Th, Tc, H, d, dtype, workspace,
+                                  workspace_bytes, stream);
+  if (r != RR_OK) return r;
+  return rr_cand_only_run(q_cand, k_hist, v_hist, k_cand, v_cand, o_cand, B, Th, Tc, H, d, dtype,
+                          scale, workspace, workspace_bytes, stream);
+}
+
+int rr_validate_jagged(const int32_t* offsets, const int32_t* cand_start, int32_t B, int32_t T,
+                       int32_t* err_flags, hipStream_t stream) {
+  if (B < 0 || T < 0) return RR_EINVAL;
+  if (!offsets || !err_flags) return RR_EINVAL;
+  return status_of(launch_validate(offsets, cand_start, B, T, err_flags, stream));
+}
+
+}  // extern "C"

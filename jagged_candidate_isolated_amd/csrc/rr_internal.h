@@ -1,0 +1,169 @@
+// Internal declarations shared by the librr translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rr.h"
+
+namespace rr {
+
+// Query-row tile heights of the attention kernels.  The work-list and the
+// workspace are sized with the smallest one.
+constexpr int kBmSimple = 64;    // fp32 (and bf16 d=16) VALU kernel: one wave, one row per lane
+constexpr int kBmMfma = 128;     // bf16 MFMA kernel: four waves of 32 query rows
+constexpr int kBmMin = 64;
+constexpr int kHeadSlots = 1024; // work items pack the head into 10 bits ...
+constexpr int kZeroHead = 1023;  // ... and head 1023 marks "zero these padding rows"
+constexpr int kMaxHeads = 1023;
+constexpr int kSortMax = 4096;   // users sorted in LDS by the work-list builder
+
+// What one user contributes to an attention call.  Query and key lists are
+// either plain row ranges or, when `idx` is used, ranges of an index array that
+// lists the rows (the compacted valid rows of a padded batch).
+struct UserMeta {
+  int32_t q_begin;   // first entry of the query list
+  int32_t n_q;       // query rows
+  int32_t kv_begin;  // first entry of the key list
+  int32_t n_kv;      // keys every query of the user reads (segment-1 / frozen rows)
+  int32_t cand_rel;  // query-list position of the first candidate (self-term from here on)
+  int32_t n_pad;     // padding rows (segment 0), listed in idx right after the query list
+  int32_t spare0, spare1;
+};
+static_assert(sizeof(UserMeta) == 32, "UserMeta is 32 bytes");
+
+// Work item: user b, head h, query tile qt; packed as {b, (qt << 10) | h}.
+__host__ __device__ inline int item_head(int2 it) { return it.y & (kHeadSlots - 1); }
+__host__ __device__ inline int item_tile(int2 it) { return it.y >> 10; }
+
+// Written by the planning kernels at the start of the workspace; the attention
+// kernels check it against their own launch so a plan made for other sizes is
+// never used.
+struct PlanHeader {
+  int32_t n_items;
+  int32_t indexed;   // query/key lists go through idx[]
+  int32_t B;
+  int32_t H;
+  int32_t bm;
+  int32_t mode;      // 0 full sequence, 1 candidate-only
+  int32_t rows;      // T (full) or Tc (candidate-only)
+  int32_t magic;
+};
+constexpr int32_t kPlanMagic = 0x52525031;  // "RRP1"
+
+// Workspace layout (every part 256-byte aligned).
+struct WsLayout {
+  size_t header;     // PlanHeader
+  size_t meta;       // UserMeta[B]
+  size_t start;      // int32[B + 1] item starts per sorted user
+  size_t idx;        // int32[T] compacted row lists
+  size_t items;      // int2[item_bound]
+  size_t total;
+  int64_t item_bound;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workgroups of an attention launch for tile height bm: one per possible work item.
+inline int64_t attn_grid(int64_t B, int64_t rows, int64_t H, int bm) {
+  return (H + 1) * ((rows + bm - 1) / bm + B);
+}
+
+inline int64_t item_upper_bound(int64_t B, int64_t rows, int64_t H) {
+  // sum_b ceil(n_b / BM) <= rows / BM + B for any split of `rows` over B users;
+  // H attention items per query tile plus at most one zeroing item per padding tile
+  return (H + 1) * ((rows + kBmMin - 1) / kBmMin + B);
+}
+
+inline WsLayout ws_layout(int64_t B, int64_t T_idx, int64_t q_rows, int64_t H) {
+  WsLayout w{};
+  size_t off = 0;
+  w.header = off; off += 256;
+  w.meta = off; off = align256(off + sizeof(UserMeta) * size_t(B));
+  w.start = off; off = align256(off + sizeof(int32_t) * size_t(B + 1));
+  w.idx = off; off = align256(off + sizeof(int32_t) * size_t(T_idx));
+  w.item_bound = item_upper_bound(B, q_rows, H);
+  w.items = off; off = align256(off + sizeof(int2) * size_t(w.item_bound));
+  w.total = off;
+  return w;
+}
+
+// Arguments of the attention kernels.
+struct AttnArgs {
+  const void* q;       // query rows
+  const void* k;       // key rows read by every query of the user
+  const void* v;
+  const void* k_self;  // own key/value of a candidate, at the query's row
+  const void* v_self;
+  void* o;
+  const PlanHeader* plan;
+  const UserMeta* meta;
+  const int32_t* idx;  // row lists (used when plan->indexed)
+  const int2* items;
+  int32_t B;
+  int32_t H;
+  int32_t mode;
+  int32_t rows;
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+// The plan in the workspace matches this launch.
+__device__ __forceinline__ bool plan_matches(const AttnArgs& a, int bm) {
+  const PlanHeader& p = *a.plan;
+  return p.magic == kPlanMagic && p.B == a.B && p.H == a.H && p.bm == bm && p.mode == a.mode &&
+         p.rows == a.rows;
+}
+
+// Segment-ID rule of one row (candidate isolation mask page, segment-ID section).
+__device__ __forceinline__ int8_t segment_of(int row, int cand_start, const uint8_t* valid,
+                                             int attend_padded_history) {
+  const bool is_candidate = row >= cand_start;
+  bool ok = valid ? (valid[row] != 0) : true;
+  if (attend_padded_history) ok = ok || !is_candidate;
+  return ok ? (is_candidate ? int8_t(-1) : int8_t(1)) : int8_t(0);
+}
+
+// Launch a kernel that takes one parameter struct; returns the launch status
+// (hipLaunchKernel reports it directly, so no sticky last-error is read or cleared).
+template <typename P>
+inline hipError_t launch1(void (*k)(P), int64_t grid, int block, hipStream_t s, P params) {
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {&params};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(static_cast<unsigned>(grid)),
+                         dim3(block), args, 0, s);
+}
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_segment_ids(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                              int flag, int B, int T, int8_t* seg, hipStream_t s);
+hipError_t launch_bounds(const int32_t* offsets, const int8_t* seg, int B, int T, int32_t* out,
+                         hipStream_t s);
+hipError_t launch_validate(const int32_t* offsets, const int32_t* cand_start, int B, int T,
+                           int32_t* err, hipStream_t s);
+hipError_t launch_compact(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                          int flag, int B, int T, UserMeta* meta, int32_t* idx, hipStream_t s);
+// mode 0: full sequence from offsets/cand_start (meta_ready: meta already written by compact)
+// mode 1: candidate-only from hist_offsets/cand_offsets
+hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_b, int meta_ready,
+                           int B, int H, int bm, int rows, int kv_rows, int cap, UserMeta* meta,
+                           int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
+hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, int d, int64_t grid, hipStream_t s);
+
+// Zero the output rows of a padding tile: rows idx[q_begin + n_q + qt*bm ...], every head.
+// `nthreads` threads of the workgroup cooperate; rows are `row_bytes` long (a multiple of 16).
+__device__ __forceinline__ void zero_padding_tile(const AttnArgs& a, const UserMeta& um, int qt,
+                                                  int bm, int row_bytes, int tid, int nthreads) {
+  const int first = qt * bm;
+  const int nrows = min(bm, um.n_pad - first);
+  const int chunks = row_bytes / 16;
+  uint4* o = static_cast<uint4*>(a.o);
+  for (int e = tid; e < nrows * chunks; e += nthreads) {
+    const int r = a.idx[um.q_begin + um.n_q + first + e / chunks];
+    o[static_cast<int64_t>(r) * chunks + (e % chunks)] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+}  // namespace rr

@@ -1,0 +1,300 @@
+"""Python binding of librr: the C ABI's calls under the same names.
+
+Argument marshalling only -- every step of the computation runs in librr's HIP
+kernels.  PyTorch supplies device memory and the current stream.  Importing this
+module fails loudly when librr.so has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librr.so")
+
+RR_OK, RR_EINVAL, RR_EDTYPE, RR_EUNSUPPORTED, RR_EWORKSPACE, RR_EHIP = 0, -1, -2, -3, -4, -5
+RR_F32, RR_BF16 = 0, 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "rr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rr_abi_version": (ctypes.c_int, []),
+    "rr_segment_ids": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, _I, _I, _P, _P]),
+    "rr_bounds": (ctypes.c_int, [_P, _P, _I, _I, _P, _P]),
+    "rr_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "rr_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I, _I, _I, _I,
+                                   ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_cand_only_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "rr_cand_only_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                             ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_validate_jagged": (ctypes.c_int, [_P, _P, _I, _I, _P, _P]),
+    "rr_attn_plan": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int, _P,
+                                    ctypes.c_size_t, _P]),
+    "rr_attn_run": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float, _P,
+                                   ctypes.c_size_t, _P]),
+    "rr_cand_only_plan": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P,
+                                         ctypes.c_size_t, _P]),
+    "rr_cand_only_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
+                                        ctypes.c_float, _P, ctypes.c_size_t, _P]),
+}
+
+
+def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m jagged_candidate_isolated_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+LIBRARY_PATH = _LIB_PATH
+
+
+class RRError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_lib.rr_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != RR_OK:
+        raise RRError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rr_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RR_F32
+    if t.dtype == torch.bfloat16:
+        return RR_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def rr_segment_ids(offsets, cand_start, valid=None, attend_padded_history=False, out=None,
+                   T: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Per-row segment IDs (int8 [T]).  ``T`` defaults to ``valid.numel()`` or ``out.numel()``;
+    otherwise it must be given (the library never reads sizes back from the device)."""
+    dev = offsets.device
+    _need(offsets, "offsets", torch.int32)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if valid is not None:
+        _need(valid, "valid", torch.uint8, dev)
+    if T is None:
+        T = valid.numel() if valid is not None else (out.numel() if out is not None else None)
+    if T is None:
+        raise ValueError("T is required")
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty(T, dtype=torch.int8, device=dev)
+    _need(out, "out", torch.int8, dev)
+    _check("rr_segment_ids", _lib.rr_segment_ids(_ptr(offsets), _ptr(cand_start), _ptr(valid),
+                                                 int(bool(attend_padded_history)), B, T, _ptr(out),
+                                                 _stream(stream, dev)))
+    return out
+
+
+def rr_bounds(offsets, seg, out=None, stream=None) -> torch.Tensor:
+    """Per-user [hist_lo, hist_hi, cand_lo, cand_hi] as int32 [4, B]."""
+    dev = offsets.device
+    _need(offsets, "offsets", torch.int32)
+    _need(seg, "seg", torch.int8, dev)
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((4, B), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, dev)
+    _check("rr_bounds", _lib.rr_bounds(_ptr(offsets), _ptr(seg), B, seg.numel(), _ptr(out),
+                                       _stream(stream, dev)))
+    return out
+
+
+def rr_attn_workspace_bytes(B: int, T: int, H: int, d: int) -> int:
+    return int(_lib.rr_attn_workspace_bytes(B, T, H, d))
+
+
+def rr_cand_only_workspace_bytes(B: int, Th: int, Tc: int, H: int, d: int) -> int:
+    return int(_lib.rr_cand_only_workspace_bytes(B, Th, Tc, H, d))
+
+
+def _workspace(nbytes: int, workspace, dev) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    return workspace
+
+
+def rr_attn_fwd(q, k, v, offsets, cand_start, valid=None, attend_padded_history=False, scale=None,
+                out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Full-sequence candidate-isolated attention.  q, k, v: [T, H, d] float32 or bfloat16."""
+    dev = q.device
+    _need(q, "q")
+    dt = _rr_dtype(q)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, q.dtype, dev)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d]")
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if valid is not None:
+        _need(valid, "valid", torch.uint8, dev)
+    T, H, d = q.shape
+    B = offsets.numel() - 1
+    if cand_start.numel() != B:
+        raise ValueError("cand_start must have B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    ws_bytes = rr_attn_workspace_bytes(B, T, H, d)
+    ws = _workspace(ws_bytes, workspace, dev)
+    _check("rr_attn_fwd", _lib.rr_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(offsets), _ptr(cand_start), _ptr(valid),
+        int(bool(attend_padded_history)), B, T, H, d, dt, float(scale or 0.0), _ptr(ws),
+        ws.numel(), _stream(stream, dev)))
+    return out
+
+
+def rr_cand_only_attn_fwd(q_cand, k_hist, v_hist, k_cand, v_cand, hist_offsets, cand_offsets,
+                          scale=None, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Candidate-only layer attention.  Candidate tensors [Tc, H, d], history K/V [Th, H, d]."""
+    dev = q_cand.device
+    _need(q_cand, "q_cand")
+    dt = _rr_dtype(q_cand)
+    if q_cand.dim() != 3:
+        raise ValueError("q_cand must be [Tc, H, d]")
+    Tc, H, d = q_cand.shape
+    for name, t in (("k_cand", k_cand), ("v_cand", v_cand)):
+        _need(t, name, q_cand.dtype, dev)
+        if t.shape != q_cand.shape:
+            raise ValueError(f"{name} shape mismatch")
+    for name, t in (("k_hist", k_hist), ("v_hist", v_hist)):
+        _need(t, name, q_cand.dtype, dev)
+        if t.dim() != 3 or t.shape[1:] != q_cand.shape[1:]:
+            raise ValueError(f"{name} must be [Th, H, d]")
+    if k_hist.shape != v_hist.shape:
+        raise ValueError("k_hist and v_hist differ in shape")
+    Th = k_hist.shape[0]
+    _need(hist_offsets, "hist_offsets", torch.int32, dev)
+    _need(cand_offsets, "cand_offsets", torch.int32, dev)
+    B = cand_offsets.numel() - 1
+    if hist_offsets.numel() != B + 1:
+        raise ValueError("hist_offsets and cand_offsets must both have B+1 entries")
+    if out is None:
+        out = torch.empty_like(q_cand)
+    _need(out, "out", q_cand.dtype, dev)
+    ws_bytes = rr_cand_only_workspace_bytes(B, Th, Tc, H, d)
+    ws = _workspace(ws_bytes, workspace, dev)
+    _check("rr_cand_only_attn_fwd", _lib.rr_cand_only_attn_fwd(
+        _ptr(q_cand), _ptr(k_hist), _ptr(v_hist), _ptr(k_cand), _ptr(v_cand), _ptr(out),
+        _ptr(hist_offsets), _ptr(cand_offsets), B, Th, Tc, H, d, dt, float(scale or 0.0),
+        _ptr(ws), ws.numel(), _stream(stream, dev)))
+    return out
+
+
+def rr_attn_plan(offsets, cand_start, T: int, H: int, d: int, dtype, valid=None,
+                 attend_padded_history=False, workspace=None, stream=None) -> torch.Tensor:
+    """Plan a full-sequence call (lengths only); returns the workspace holding the plan."""
+    dev = offsets.device
+    _need(offsets, "offsets", torch.int32)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if valid is not None:
+        _need(valid, "valid", torch.uint8, dev)
+    B = offsets.numel() - 1
+    dt = _rr_dtype(torch.empty(0, dtype=dtype))
+    ws = _workspace(rr_attn_workspace_bytes(B, T, H, d), workspace, dev)
+    _check("rr_attn_plan", _lib.rr_attn_plan(_ptr(offsets), _ptr(cand_start), _ptr(valid),
+                                             int(bool(attend_padded_history)), B, T, H, d, dt,
+                                             _ptr(ws), ws.numel(), _stream(stream, dev)))
+    return ws
+
+
+def rr_attn_run(q, k, v, B: int, workspace, scale=None, out=None, stream=None) -> torch.Tensor:
+    """Attention with the plan in ``workspace`` (same sizes as the plan)."""
+    dev = q.device
+    _need(q, "q")
+    dt = _rr_dtype(q)
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    T, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    _check("rr_attn_run", _lib.rr_attn_run(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, d, dt,
+                                           float(scale or 0.0), _ptr(workspace), workspace.numel(),
+                                           _stream(stream, dev)))
+    return out
+
+
+def rr_cand_only_plan(hist_offsets, cand_offsets, Th: int, Tc: int, H: int, d: int, dtype,
+                      workspace=None, stream=None) -> torch.Tensor:
+    dev = cand_offsets.device
+    _need(hist_offsets, "hist_offsets", torch.int32, dev)
+    _need(cand_offsets, "cand_offsets", torch.int32, dev)
+    B = cand_offsets.numel() - 1
+    dt = _rr_dtype(torch.empty(0, dtype=dtype))
+    ws = _workspace(rr_cand_only_workspace_bytes(B, Th, Tc, H, d), workspace, dev)
+    _check("rr_cand_only_plan", _lib.rr_cand_only_plan(_ptr(hist_offsets), _ptr(cand_offsets), B, Th,
+                                                       Tc, H, d, dt, _ptr(ws), ws.numel(),
+                                                       _stream(stream, dev)))
+    return ws
+
+
+def rr_cand_only_run(q_cand, k_hist, v_hist, k_cand, v_cand, B: int, workspace, scale=None, out=None,
+                     stream=None) -> torch.Tensor:
+    dev = q_cand.device
+    _need(q_cand, "q_cand")
+    dt = _rr_dtype(q_cand)
+    for name, t in (("k_hist", k_hist), ("v_hist", v_hist), ("k_cand", k_cand), ("v_cand", v_cand)):
+        _need(t, name, q_cand.dtype, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    Tc, H, d = q_cand.shape
+    Th = k_hist.shape[0]
+    if out is None:
+        out = torch.empty_like(q_cand)
+    _need(out, "out", q_cand.dtype, dev)
+    _check("rr_cand_only_run", _lib.rr_cand_only_run(
+        _ptr(q_cand), _ptr(k_hist), _ptr(v_hist), _ptr(k_cand), _ptr(v_cand), _ptr(out), B, Th, Tc, H,
+        d, dt, float(scale or 0.0), _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return out
+
+
+def rr_validate_jagged(offsets, cand_start, T: int, stream=None) -> int:
+    """Debug: data-contract bit flags (0 = fine).  Synchronises the stream to read them."""
+    dev = offsets.device
+    _need(offsets, "offsets", torch.int32)
+    if cand_start is not None:
+        _need(cand_start, "cand_start", torch.int32, dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = _stream(stream, dev)
+    _check("rr_validate_jagged", _lib.rr_validate_jagged(_ptr(offsets), _ptr(cand_start),
+                                                         offsets.numel() - 1, T, _ptr(err), s))
+    return int(err.item())

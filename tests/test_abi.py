@@ -1,0 +1,125 @@
+"""The C ABI on the host (CPU only): the library loads, exports every declared symbol,
+and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rr.h")
+
+
+def _lib():
+    from jagged_candidate_isolated_amd import rr
+    return rr, rr._lib
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("rr_segment_ids", "rr_bounds", "rr_attn_fwd", "rr_cand_only_attn_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    _, lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    rr, lib = _lib()
+    assert lib.rr_abi_version() == 1
+    for st in (rr.RR_OK, rr.RR_EINVAL, rr.RR_EDTYPE, rr.RR_EUNSUPPORTED, rr.RR_EWORKSPACE, rr.RR_EHIP):
+        assert lib.rr_status_string(st)
+    assert lib.rr_status_string(-99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below returns before any launch
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, offsets=FAKE, cand_start=FAKE, valid=None, flag=0,
+             B=2, T=10, H=2, d=64, dtype=1, scale=0.0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.rr_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["offsets"], a["cand_start"], a["valid"],
+                           a["flag"], a["B"], a["T"], a["H"], a["d"], a["dtype"], a["scale"], a["ws"],
+                           a["ws_bytes"], a["stream"])
+
+
+def test_attn_argument_errors():
+    rr, lib = _lib()
+    assert _attn(lib, B=-1) == rr.RR_EINVAL
+    assert _attn(lib, T=-5) == rr.RR_EINVAL
+    assert _attn(lib, dtype=7) == rr.RR_EDTYPE
+    for d in (0, 8, 48, 96, 256):
+        assert _attn(lib, d=d) == rr.RR_EUNSUPPORTED, d
+    assert _attn(lib, H=2000) == rr.RR_EUNSUPPORTED
+    assert _attn(lib, q=None) == rr.RR_EINVAL
+    assert _attn(lib, offsets=None) == rr.RR_EINVAL
+    assert _attn(lib, cand_start=None) == rr.RR_EINVAL
+    assert _attn(lib, ws=None) == rr.RR_EWORKSPACE
+    need = lib.rr_attn_workspace_bytes(2, 10, 2, 64)
+    assert need > 0
+    assert _attn(lib, ws_bytes=need - 1) == rr.RR_EWORKSPACE
+    # empty calls are valid no-ops, even with NULL tensors
+    assert _attn(lib, B=0, q=None, k=None, v=None, o=None, ws=None) == rr.RR_OK
+    assert _attn(lib, T=0, q=None, ws=None) == rr.RR_OK
+
+
+def test_cand_only_argument_errors():
+    rr, lib = _lib()
+    f = lib.rr_cand_only_attn_fwd
+
+    def call(**kw):
+        a = dict(qc=FAKE, kh=FAKE, vh=FAKE, kc=FAKE, vc=FAKE, oc=FAKE, ho=FAKE, co=FAKE, B=2, Th=10,
+                 Tc=6, H=2, d=128, dtype=1, scale=0.0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return f(a["qc"], a["kh"], a["vh"], a["kc"], a["vc"], a["oc"], a["ho"], a["co"], a["B"],
+                 a["Th"], a["Tc"], a["H"], a["d"], a["dtype"], a["scale"], a["ws"], a["ws_bytes"],
+                 a["stream"])
+    assert call(Th=-1) == rr.RR_EINVAL
+    assert call(dtype=5) == rr.RR_EDTYPE
+    assert call(d=80) == rr.RR_EUNSUPPORTED
+    assert call(kh=None) == rr.RR_EINVAL
+    assert call(kh=None, vh=None, Th=0, ws=None) == rr.RR_EWORKSPACE
+    assert call(ws=None) == rr.RR_EWORKSPACE
+    assert call(co=None) == rr.RR_EINVAL
+    assert call(Tc=0, qc=None, ws=None) == rr.RR_OK
+    assert lib.rr_cand_only_workspace_bytes(2, 10, 6, 2, 128) > 0
+    assert lib.rr_cand_only_workspace_bytes(2, 10, 6, 2, 100) == 0
+
+
+def test_segment_and_bounds_argument_errors():
+    rr, lib = _lib()
+    assert lib.rr_segment_ids(FAKE, FAKE, None, 0, -1, 5, FAKE, None) == rr.RR_EINVAL
+    assert lib.rr_segment_ids(None, FAKE, None, 0, 2, 5, FAKE, None) == rr.RR_EINVAL
+    assert lib.rr_segment_ids(FAKE, FAKE, None, 0, 2, 5, None, None) == rr.RR_EINVAL
+    assert lib.rr_segment_ids(None, None, None, 0, 0, 0, None, None) == rr.RR_OK
+    assert lib.rr_bounds(FAKE, None, 2, 5, FAKE, None) == rr.RR_EINVAL
+    assert lib.rr_bounds(FAKE, FAKE, 2, 5, None, None) == rr.RR_EINVAL
+    assert lib.rr_bounds(None, None, 0, 0, None, None) == rr.RR_OK
+    assert lib.rr_validate_jagged(None, None, 1, 1, FAKE, None) == rr.RR_EINVAL
+
+
+def test_workspace_size_grows_with_work():
+    _, lib = _lib()
+    a = lib.rr_attn_workspace_bytes(64, 16000, 4, 64)
+    b = lib.rr_attn_workspace_bytes(64, 32000, 4, 64)
+    assert 0 < a < b
+    assert lib.rr_attn_workspace_bytes(-1, 10, 1, 64) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    rr, _ = _lib()
+    q = torch.zeros(4, 1, 16)
+    off = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        rr.rr_attn_fwd(q, q, q, off, torch.tensor([2], dtype=torch.int32))
