@@ -42,10 +42,6 @@ constexpr int kBm = kWaves * kQw;        // query rows per work item
 static_assert(kBm == kBmMfma, "tile height");
 constexpr int kThreads = kWaves * 64;
 
-__device__ __forceinline__ int swap23(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -55,19 +51,58 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+// LDS tile layout.  A K or V tile is BN rows of D bf16 (row-major), stored in
+// 16-byte chunks; chunk c of row r sits at position c ^ swz(r) of that row.  The
+// swizzle keeps both kinds of reads free of bank conflicts: the K reads (16
+// consecutive rows, one chunk each) and the transposed V reads (4 consecutive rows,
+// 4 chunks each) touch distinct banks.  Tiles arrive by direct-to-LDS loads: lane l
+// of a load writes LDS slot l, so the swizzle is applied by choosing which global
+// chunk each lane fetches.
+template <int CH>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CH == 16) return 4 * (row & 3) + ((row >> 2) & 3);
+  else if constexpr (CH == 8) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  else return (row >> 2) & 3;   // CH == 4: 64-byte rows
+}
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// V^T operand of the PV product for k-step ks and output block db: eight keys of one
+// V column per lane, read with two transposed LDS loads.  Within each 16-lane group
+// the transposed load returns, in lane j, element j%4 of the 8-byte pieces addressed
+// by lanes 4k + j/4 (k = 0..3); each lane therefore addresses row (key) 4*half + s/4
+// at columns 4*(s%4)..+3 of its group's 16 columns, and gets one column, four keys.
+template <int D>
+__device__ __forceinline__ bf16x8 read_vt(const u16* __restrict__ sv, int ks, int db, int lane) {
+  constexpr int CH = D / 8;
+  const int s = lane & 15, grp = (lane >> 4) & 1, half = lane >> 5;
+  const int col = db * 32 + 16 * grp + 4 * (s & 3);      // first of 4 columns (elements)
+  const int c = col >> 3, sub = (col & 7) * 2;           // 16-byte chunk, byte offset in it
+  v4i16 r[2];
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const int row = ks * 16 + 8 * part + 4 * half + (s >> 2);
+    const int p = c ^ swz<CH>(row);
+    LDS_AS char* addr = (LDS_AS char*)(sv) + (row * CH + p) * 16 + sub;   // generic -> LDS address space
+    r[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)addr);
+  }
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 w = {r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 template <int D, int BN, bool INDEXED>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16* __restrict__ s_k,
                                           u16* __restrict__ s_v) {
-  constexpr int KSTR = D + 8;             // K tile row stride (elements); +16 B staggers LDS banks
-  constexpr int VSTR = BN + 8;            // V^T tile row stride
-  constexpr int KK = D / 16;              // k-steps of S^T
-  constexpr int KB = BN / 32;             // 32-key blocks per tile
-  constexpr int DB = D / 32;              // 32-wide blocks of O^T
-  constexpr int KCH = BN * D / 8;         // 16-byte chunks of a K tile
-  constexpr int KCH_T = (KCH + kThreads - 1) / kThreads;
-  constexpr int VBLK = (BN / 4) * (D / 8);  // 4-key x 8-element blocks of a V tile
-  constexpr int VBLK_T = (VBLK + kThreads - 1) / kThreads;
-  static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE = BN * D;               // elements per K (or V) tile
+  constexpr int LOADS = TILE * 2 / (kThreads * 16);   // direct-to-LDS loads per thread per tile
+  constexpr int KK = D / 16;                 // k-steps of S^T
+  constexpr int KB = BN / 32;                // 32-key blocks per tile
+  constexpr int DB = D / 32;                 // 32-wide blocks of O^T
+  static_assert(D % 32 == 0 && BN % 32 == 0 && LOADS >= 1 && TILE * 2 % (kThreads * 16) == 0,
+                "tile shape");
 
   const int b = it.x, h = item_head(it), qt = item_tile(it);
   const UserMeta um = a.meta[b];
@@ -89,6 +124,29 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   const int qe = um.q_begin + min(qpos, um.n_q - 1);
   const int qrow = INDEXED ? a.idx[qe] : qe;
 
+  const int n_kv = um.n_kv;
+  const int ntiles = (n_kv + BN - 1) / BN;
+
+  // Issue the direct-to-LDS loads of key/value tile t into buffer t & 1.  Load i of
+  // wave w fills LDS slots (w*LOADS + i)*64 + lane; slot -> (row, chunk position).
+  auto issue_tile = [&](int t) {
+    u16* dk = s_k + (t & 1) * TILE;
+    u16* dv = s_v + (t & 1) * TILE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot = (wave * LOADS + i) * 64 + lane;
+      const int row = slot / CH, p = slot % CH;
+      const int c = p ^ swz<CH>(row);
+      const int e = um.kv_begin + min(t * BN + row, n_kv - 1);   // clamp the tail into the list
+      const int64_t g = static_cast<int64_t>(INDEXED ? a.idx[e] : e) * rs + c * 8;
+      const int lds_off = (wave * LOADS + i) * 64 * 8;           // elements; one load = 1 KiB
+      __builtin_amdgcn_global_load_lds(Kp + g, (LDS_AS void*)(dk + lds_off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vp + g, (LDS_AS void*)(dv + lds_off), 16, 0, 0);
+    }
+  };
+
+  if (ntiles > 0) issue_tile(0);
+
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
@@ -99,82 +157,23 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
 
-  const int n_kv = um.n_kv;
-  const int ntiles = (n_kv + BN - 1) / BN;
-
-  uint4 kst[KCH_T];
-  uint4 vst[VBLK_T][4];
-
-  auto key_row = [&](int j) {
-    const int e = um.kv_begin + min(j, n_kv - 1);   // clamp the tail into the key list
-    return INDEXED ? a.idx[e] : e;
-  };
-  auto load_tile = [&](int t) {
+  // per-lane parts of the K operand addresses (rows kb*32 + ql)
+  int k_row_off[KB], k_mask[KB];
 #pragma unroll
-    for (int i = 0; i < KCH_T; ++i) {
-      const int c = tid + kThreads * i;
-      if (KCH % kThreads == 0 || c < KCH) {
-        const int r = c / (D / 8), c8 = c % (D / 8);
-        kst[i] = *reinterpret_cast<const uint4*>(Kp + key_row(t * BN + r) * rs + c8 * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VBLK_T; ++i) {
-      const int vb = tid + kThreads * i;
-      if (VBLK % kThreads == 0 || vb < VBLK) {
-        const int g = vb % (BN / 4), c8 = vb / (BN / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vst[i][r] = *reinterpret_cast<const uint4*>(Vp + key_row(t * BN + 4 * g + r) * rs + c8 * 8);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH_T; ++i) {
-      const int c = tid + kThreads * i;
-      if (KCH % kThreads == 0 || c < KCH) {
-        const int r = c / (D / 8), c8 = c % (D / 8);
-        *reinterpret_cast<uint4*>(&s_k[r * KSTR + c8 * 8]) = kst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VBLK_T; ++i) {
-      const int vb = tid + kThreads * i;
-      if (VBLK % kThreads == 0 || vb < VBLK) {
-        const int g = vb % (BN / 4), c8 = vb / (BN / 4);
-        const int kv0 = 4 * g;
-        const int col = (kv0 & ~15) | swap23(kv0 & 15);   // 4 keys stay contiguous
-        const unsigned w0[4] = {vst[i][0].x, vst[i][0].y, vst[i][0].z, vst[i][0].w};
-        const unsigned w1[4] = {vst[i][1].x, vst[i][1].y, vst[i][1].z, vst[i][1].w};
-        const unsigned w2[4] = {vst[i][2].x, vst[i][2].y, vst[i][2].z, vst[i][2].w};
-        const unsigned w3[4] = {vst[i][3].x, vst[i][3].y, vst[i][3].z, vst[i][3].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int wi = e >> 1;
-          unsigned lo, hi;
-          if (e & 1) {
-            lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-            hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-          } else {
-            lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-            hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-          }
-          *reinterpret_cast<uint2*>(&s_v[(c8 * 8 + e) * VSTR + col]) = make_uint2(lo, hi);
-        }
-      }
-    }
-  };
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile();
+  for (int kb = 0; kb < KB; ++kb) {
+    const int row = kb * 32 + ql;
+    k_row_off[kb] = row * CH;
+    k_mask[kb] = swz<CH>(row) ^ half;
   }
-  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);   // next tile's global loads overlap this tile's math
+    // tile t has landed (this wave's loads) and is visible (every wave's, after the
+    // barrier); the barrier also tells that every wave is done with buffer (t+1)&1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(t + 1);   // overlaps this tile's math
+    const u16* sk = s_k + (t & 1) * TILE;
+    const u16* sv = s_v + (t & 1) * TILE;
 
     // S^T = K Q^T for this wave's 32 queries
     f32x16 sacc[KB];
@@ -183,8 +182,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
       sacc[kb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&s_k[(kb * 32 + ql) * KSTR + 16 * kk + 8 * half]);
+        const int p = (2 * kk) ^ k_mask[kb];
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + (k_row_off[kb] + p) * 8);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
       }
     }
@@ -197,25 +196,43 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
           if (j >= n_kv) sacc[kb][r] = -INFINITY;
         }
     }
-    // online softmax, one query per lane (key halves split across the lane halves)
-    float mx = -INFINITY;
+    // online softmax, one query per lane (key halves split across the lane halves);
+    // max and sum as trees to keep the dependency chains short
+    float mx[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      float m4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx * sl2);
+      for (int g = 0; g < 4; ++g)
+        m4[g] = fmaxf(fmaxf(sacc[kb][4 * g], sacc[kb][4 * g + 1]),
+                      fmaxf(sacc[kb][4 * g + 2], sacc[kb][4 * g + 3]));
+      mx[kb] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    }
+#pragma unroll
+    for (int w = 1; w < KB; w <<= 1)
+#pragma unroll
+      for (int kb = 0; kb + w < KB; kb += 2 * w) mx[kb] = fmaxf(mx[kb], mx[kb + w]);
+    float tmax = fmaxf(mx[0], __shfl_xor(mx[0], 32));
+    const float m_new = fmaxf(m_i, tmax * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
-    float ls = 0.f;
+    float ls[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      float s4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m_new));
-        sacc[kb][r] = p;
-        ls += p;
+      for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int r = 4 * g; r < 4 * g + 4; ++r)
+          sacc[kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m_new));
+        s4[g] = (sacc[kb][4 * g] + sacc[kb][4 * g + 1]) + (sacc[kb][4 * g + 2] + sacc[kb][4 * g + 3]);
       }
-    l_i = l_i * alpha + ls;
+      ls[kb] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    }
+#pragma unroll
+    for (int w = 1; w < KB; w <<= 1)
+#pragma unroll
+      for (int kb = 0; kb + w < KB; kb += 2 * w) ls[kb] += ls[kb + w];
+    l_i = l_i * alpha + ls[0];
     m_i = m_new;
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -229,16 +246,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(sacc[kb][s8 + j]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&s_v[(db * 32 + ql) * VSTR + 16 * ks + 8 * half]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-    if (more) {
-      store_tile();
-      __syncthreads();
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_vt<D>(sv, ks, db, lane), pf, oacc[db],
+                                                           0, 0, 0);
     }
   }
 
@@ -288,12 +298,14 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
         *reinterpret_cast<uint2*>(Op + qrow * rs + db * 32 + 8 * g + 4 * half) = w;
       }
   }
+  // no wave may leave while others still read LDS tiles it helped load (the loads
+  // are complete once every wave passed the last in-loop barrier), nothing to wait for
 }
 
 template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_mfma(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 s_k[BN * (D + 8)];
-  __shared__ __attribute__((aligned(16))) u16 s_v[D * (BN + 8)];
+  __shared__ __attribute__((aligned(16))) u16 s_k[2 * BN * D];   // double-buffered K tiles
+  __shared__ __attribute__((aligned(16))) u16 s_v[2 * BN * D];   // double-buffered V tiles
   if (!plan_matches(a, kBm)) return;
   const int item = blockIdx.x;
   if (item >= a.plan->n_items) return;

@@ -17,7 +17,7 @@ constexpr int kBmMin = 64;
 constexpr int kHeadSlots = 1024; // work items pack the head into 10 bits ...
 constexpr int kZeroHead = 1023;  // ... and head 1023 marks "zero these padding rows"
 constexpr int kMaxHeads = 1023;
-constexpr int kSortMax = 4096;   // users sorted in LDS by the work-list builder
+constexpr int kSortMax = 2048;   // users planned (and sorted) in LDS by the work-list builder
 
 // What one user contributes to an attention call.  Query and key lists are
 // either plain row ranges or, when `idx` is used, ranges of an index array that

@@ -4,9 +4,14 @@
 // lengths), the list of attention work items: user b, head h, query tile qt.
 // Users are ordered by the number of keys their queries read, longest first
 // (longest-processing-time order), so the GPU's in-order workgroup dispatch
-// starts the expensive items first and the short ones fill the tail.  Ties keep
-// the user order.  Within a user the items go head by head, query tile by query
-// tile, so neighbouring items read the same keys and values.
+// starts the expensive items first and the short ones fill the tail.  The order
+// is a counting sort over 128 logarithmic key-count buckets (four per octave):
+// three barriers whatever the batch size, and within a bucket key counts differ
+// by less than 19%, which is all the scheduling needs.  (The order of users that
+// share a bucket may vary from call to call; it decides only which workgroup
+// computes an item, never a result, since items write disjoint rows.)  Within a
+// user the items go head by head, query tile by query tile, so neighbouring
+// items read the same keys and values.
 //
 // Prior art: the CTI inference notes (varlen flash-attention section) build a
 // block-to-sequence map on the device with a shape-derived grid upper bound and
@@ -17,7 +22,18 @@
 namespace rr {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kBuckets = 128;      // logarithmic key-count buckets of the counting sort
+
+// Bucket of a key count, longest first: bucket 0 holds the largest counts and the
+// last bucket the users without keys.  Four buckets per octave.
+__device__ __forceinline__ int cost_bucket(int cost) {
+  if (cost <= 0) return kBuckets - 1;
+  const int lg = 31 - __clz(cost);                                   // 0..30
+  const int frac = lg >= 2 ? (cost >> (lg - 2)) & 3 : (cost << (2 - lg)) & 3;
+  return kBuckets - 2 - min(lg * 4 + frac, kBuckets - 2);            // 0..126
+}
 
 struct WorklistParams {
   int mode;              // 0: full sequence (offs_a = offsets, offs_b = cand_start)
@@ -71,75 +87,102 @@ __device__ __forceinline__ UserMeta plain_meta(const WorklistParams& p, int b) {
   return m;
 }
 
-__global__ __launch_bounds__(kThreads) void k_worklist(WorklistParams p) {
-  __shared__ unsigned long long s_key[kSortMax];
-  __shared__ int s_scan[kThreads];
-  __shared__ int s_carry;
-  const int tid = threadIdx.x;
-  const bool sorted = p.B <= kSortMax;
-
-  if (!p.meta_ready) {
-    for (int b = tid; b < p.B; b += kThreads) p.meta[b] = plain_meta(p, b);
-    __syncthreads();  // the meta writes are visible to the whole workgroup after the barrier
+// Inclusive scan of one int per thread over the workgroup: shuffles within each
+// wave, one barrier for the wave totals.
+__device__ __forceinline__ int block_inclusive_scan(int x, int* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  __syncthreads();
+  return x + before;
+}
 
-  // 1. order users by key count, descending (bitonic sort of (cost, user) keys)
-  int n = 1;
-  if (sorted) {
-    while (n < p.B) n <<= 1;
-    for (int i = tid; i < n; i += kThreads) {
-      unsigned long long key = ~0ull;
-      if (i < p.B) {
-        const int cost = max(p.meta[i].n_kv, 0);
-        key = (static_cast<unsigned long long>(0x7fffffffu - static_cast<unsigned>(cost)) << 32) |
-              static_cast<unsigned>(i);
+// Users up to kSortMax are planned entirely in LDS: one global read of the offsets,
+// then the counting sort, the scan and the item writes without further global
+// round trips.  Larger batches keep the user order and read the per-user counts
+// back from `meta`.
+__global__ __launch_bounds__(kThreads) void k_worklist(WorklistParams p) {
+  __shared__ int s_order[kSortMax];      // users, longest key list first
+  __shared__ int s_nqt[kSortMax];
+  __shared__ int s_nzt[kSortMax];
+  __shared__ unsigned char s_bkt[kSortMax];
+  __shared__ int s_start[kSortMax + 1];
+  __shared__ int s_hist[kBuckets];
+  __shared__ int s_wave[kWavesPerBlock];
+  const int tid = threadIdx.x;
+  const bool in_lds = p.B <= kSortMax;
+
+  for (int i = tid; i < kBuckets; i += kThreads) s_hist[i] = 0;
+  __syncthreads();
+  // 1. per-user counts (and the meta the attention kernel reads), bucket histogram
+  for (int b = tid; b < p.B; b += kThreads) {
+    const UserMeta m = p.meta_ready ? p.meta[b] : plain_meta(p, b);
+    if (!p.meta_ready) p.meta[b] = m;
+    if (in_lds) {
+      int nqt, nzt;
+      user_items(m, p.H, p.bm, nqt, nzt);
+      s_nqt[b] = nqt;
+      s_nzt[b] = nzt;
+      const int k = cost_bucket(m.n_kv);
+      s_bkt[b] = static_cast<unsigned char>(k);
+      atomicAdd(&s_hist[k], 1);
+    }
+  }
+  __syncthreads();   // also makes the meta writes visible to the whole workgroup
+
+  // 2. counting sort: bucket offsets (one wave scans the 128 buckets), then scatter
+  if (in_lds) {
+    if (tid < 64) {
+      const int a = s_hist[2 * tid], c = s_hist[2 * tid + 1];
+      int x = a + c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (tid >= off) x += y;
       }
-      s_key[i] = key;
+      s_hist[2 * tid] = x - a - c;       // exclusive offsets
+      s_hist[2 * tid + 1] = x - c;
     }
     __syncthreads();
-    for (int k = 2; k <= n; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n; i += kThreads) {
-          const int l = i ^ j;
-          if (l > i) {
-            const unsigned long long a = s_key[i], c = s_key[l];
-            const bool up = (i & k) == 0;
-            if ((a > c) == up) { s_key[i] = c; s_key[l] = a; }
-          }
-        }
-        __syncthreads();
-      }
-    }
+    for (int b = tid; b < p.B; b += kThreads) s_order[atomicAdd(&s_hist[s_bkt[b]], 1)] = b;
+    __syncthreads();
   }
 
-  // 2. exclusive scan of the item counts in that order
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
+  // 3. exclusive scan of the item counts in that order
+  int carry = 0;
   for (int base = 0; base < p.B; base += kThreads) {
     const int r = base + tid;
     int cnt = 0;
     if (r < p.B) {
-      const int b = sorted ? static_cast<int>(s_key[r] & 0xffffffffu) : r;
-      int nqt, nzt;
-      cnt = user_items(p.meta[b], p.H, p.bm, nqt, nzt);
+      if (in_lds) {
+        const int b = s_order[r];
+        cnt = p.H * s_nqt[b] + s_nzt[b];
+      } else {
+        int nqt, nzt;
+        cnt = user_items(p.meta[r], p.H, p.bm, nqt, nzt);
+      }
     }
-    s_scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
+    const int incl = block_inclusive_scan(cnt, s_wave);
+    if (r < p.B) {
+      if (in_lds) s_start[r] = carry + incl - cnt;
+      else p.start[r] = carry + incl - cnt;
     }
-    const int carry = s_carry;
-    if (r < p.B) p.start[r] = carry + s_scan[tid] - cnt;
-    __syncthreads();
-    if (tid == kThreads - 1) s_carry = carry + s_scan[tid];
+    int block_total = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) block_total += s_wave[w];
+    carry += block_total;
     __syncthreads();
   }
-  const int total = min(s_carry, p.cap);
+  const int total = min(carry, p.cap);
   if (tid == 0) {
-    p.start[p.B] = total;
+    if (in_lds) s_start[p.B] = carry;
+    p.start[p.B] = carry;
     PlanHeader hd;
     hd.n_items = total;
     hd.indexed = p.meta_ready;
@@ -153,24 +196,43 @@ __global__ __launch_bounds__(kThreads) void k_worklist(WorklistParams p) {
   }
   __syncthreads();
 
-  // 3. write the items: one wave per user
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int r = wave; r < p.B; r += kThreads / 64) {
-    const int b = sorted ? static_cast<int>(s_key[r] & 0xffffffffu) : r;
-    int nqt, nzt;
-    const int cnt = user_items(p.meta[b], p.H, p.bm, nqt, nzt);
+  // 4. write the items: thread t writes one contiguous run of the item list, so no
+  //    thread waits on another user's row; within a user, heads outer and query
+  //    tiles inner, then the padding tiles to zero
+  const int per = (total + kThreads - 1) / kThreads;
+  const int i0 = tid * per, i1 = min(i0 + per, total);
+  if (i0 >= i1) return;
+  auto start_of = [&](int r) { return in_lds ? s_start[r] : p.start[r]; };
+  int lo = 0, hi = p.B;   // last sorted user r with start_of(r) <= i0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (start_of(mid) <= i0) lo = mid; else hi = mid;
+  }
+  int r = lo;
+  for (int i = i0; i < i1;) {
+    const int s0 = start_of(r), s1 = start_of(r + 1);
+    if (i >= s1) { ++r; continue; }
+    int b, nqt, nzt;
+    if (in_lds) {
+      b = s_order[r];
+      nqt = s_nqt[b];
+      nzt = s_nzt[b];
+    } else {
+      b = r;
+      user_items(p.meta[b], p.H, p.bm, nqt, nzt);
+    }
     const int n_attn = p.H * nqt;
-    const int s0 = p.start[r];
-    for (int i = lane; i < cnt && s0 + i < total; i += 64) {
-      int h, qt;
-      if (i < n_attn) {
-        h = i / nqt;
-        qt = i - h * nqt;
+    int local = i - s0;
+    int h = 0, qt = 0;
+    if (local < n_attn) { h = local / nqt; qt = local - h * nqt; }
+    const int end = min(i1, s1);
+    for (; i < end; ++i, ++local) {
+      if (local < n_attn) {
+        p.items[i] = make_int2(b, (qt << 10) | h);
+        if (++qt == nqt) { qt = 0; ++h; }
       } else {
-        h = kZeroHead;
-        qt = i - n_attn;
+        p.items[i] = make_int2(b, ((local - n_attn) << 10) | kZeroHead);
       }
-      p.items[s0 + i] = make_int2(b, (qt << 10) | h);
     }
   }
 }
