@@ -27,6 +27,8 @@
 // Numerics: bf16 operands, fp32 accumulation, online softmax in fp32 with exp2
 // (scale * log2 e folded into one FMA), P rounded to bf16 for the PV product,
 // output rounded to bf16 (round to nearest even).
+#include <type_traits>
+
 #include "rr_internal.h"
 
 namespace rr {
@@ -68,29 +70,52 @@ __device__ __forceinline__ int swz(int row) {
 #define LDS_AS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// V^T operand of the PV product for k-step ks and output block db: eight keys of one
-// V column per lane, read with two transposed LDS loads.  Within each 16-lane group
-// the transposed load returns, in lane j, element j%4 of the 8-byte pieces addressed
-// by lanes 4k + j/4 (k = 0..3); each lane therefore addresses row (key) 4*half + s/4
-// at columns 4*(s%4)..+3 of its group's 16 columns, and gets one column, four keys.
+// V^T operand of the PV product: eight keys of one V column per lane, read with two
+// transposed LDS loads.  Within each 16-lane group the transposed load returns, in
+// lane j, element j%4 of the 8-byte pieces addressed by lanes 4k + j/4 (k = 0..3); so
+// lane s of a group addresses row (key) 4*half + s/4 at columns 4*(s%4)..+3 of the
+// group's 16 columns, and receives one column, four keys.  vt_offset() gives the
+// byte offset of that piece for k-step 0; k-step ks adds ks * 16 rows.
 template <int D>
-__device__ __forceinline__ bf16x8 read_vt(const u16* __restrict__ sv, int ks, int db, int lane) {
+__device__ __forceinline__ uint32_t vt_offset(int db, int part, int lane) {
   constexpr int CH = D / 8;
   const int s = lane & 15, grp = (lane >> 4) & 1, half = lane >> 5;
   const int col = db * 32 + 16 * grp + 4 * (s & 3);      // first of 4 columns (elements)
   const int c = col >> 3, sub = (col & 7) * 2;           // 16-byte chunk, byte offset in it
-  v4i16 r[2];
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    const int row = ks * 16 + 8 * part + 4 * half + (s >> 2);
-    const int p = c ^ swz<CH>(row);
-    LDS_AS char* addr = (LDS_AS char*)(sv) + (row * CH + p) * 16 + sub;   // generic -> LDS address space
-    r[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)addr);
-  }
+  const int row = 8 * part + 4 * half + (s >> 2);        // swz() ignores multiples of 16 rows
+  return static_cast<uint32_t>((row * CH + (c ^ swz<CH>(row))) * 16 + sub);
+}
+
+__device__ __forceinline__ bf16x8 read_vt(const char* sv, uint32_t off0, uint32_t off1) {
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(sv + off0));
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(sv + off1));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 w = {r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
+  const v8i16 w = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
   return __builtin_bit_cast(bf16x8, w);
 }
+
+// Max of three.  This file is compiled without NaN support (no value here is ever
+// NaN: scores are finite or -inf, and no expression subtracts two infinities), so
+// the compiler emits v_max3_f32 directly instead of first canonicalising each MFMA
+// result for IEEE maxNum semantics.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// Buffer resource of a raw byte range (gfx9 dword 3: 32-bit data, no swizzle); loads
+// past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Rows keep their running maximum as the softmax reference until a tile's maximum
+// exceeds it by more than 2^kLazyRescale (log2 units); only then are the row's
+// accumulator and sum rescaled.  Probabilities stay below 2^kLazyRescale, far from
+// any overflow, and each row decides for itself, so a row's result never depends
+// on the other rows of its wave.
+#ifndef RR_LAZY_RESCALE
+#define RR_LAZY_RESCALE 8.f
+#endif
+constexpr float kLazyRescale = RR_LAZY_RESCALE;
 
 template <int D, int BN, bool INDEXED>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16* __restrict__ s_k,
@@ -127,21 +152,60 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   const int n_kv = um.n_kv;
   const int ntiles = (n_kv + BN - 1) / BN;
 
-  // Issue the direct-to-LDS loads of key/value tile t into buffer t & 1.  Load i of
-  // wave w fills LDS slots (w*LOADS + i)*64 + lane; slot -> (row, chunk position).
+  // Direct-to-LDS loads of key/value tile t into buffer t & 1.  Load i of wave w fills
+  // LDS slots (w*LOADS + i)*64 + lane; slot -> (row, chunk position) -> global chunk.
+  // A full tile of a plain row list is one byte range: a buffer resource whose per-lane
+  // offsets never change between tiles.  The partial last tile, and row lists through
+  // idx[], load per row with the row index clamped into the key list (the last tile
+  // masks the repeated rows), so every byte that reaches LDS is a real key or value.
+  int ld_row[LOADS];
+  uint32_t ld_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = (wave * LOADS + i) * 64 + lane;
+    const int row = slot / CH, p = slot % CH;
+    ld_row[i] = row;
+    ld_off[i] = static_cast<uint32_t>(row * rs * 2 + (p ^ swz<CH>(row)) * 16);
+  }
+  const int64_t user_bytes = n_kv > 0 ? (static_cast<int64_t>(n_kv - 1) * rs + D) * 2 : 0;
+#ifdef RR_NO_RANGED_LOADS
+  const bool ranged = false;
+#else
+  const bool ranged = !INDEXED && user_bytes + static_cast<int64_t>(BN) * rs * 2 < (int64_t(1) << 31);
+#endif
+  const char* k_user = reinterpret_cast<const char*>(Kp) + static_cast<int64_t>(um.kv_begin) * rs * 2;
+  const char* v_user = reinterpret_cast<const char*>(Vp) + static_cast<int64_t>(um.kv_begin) * rs * 2;
   auto issue_tile = [&](int t) {
     u16* dk = s_k + (t & 1) * TILE;
     u16* dv = s_v + (t & 1) * TILE;
+    if (ranged && (t + 1) * BN <= n_kv) {
+      // a full tile: the descriptor starts at the tile and ends at the user's last key
+      // byte, so the range check also keeps every load inside the user's keys
+      const int64_t tile_off = static_cast<int64_t>(t) * BN * rs * 2;
+      const uint32_t left = static_cast<uint32_t>(user_bytes - tile_off);
+      const __amdgpu_buffer_rsrc_t k_rsrc = byte_range(k_user + tile_off, left);
+      const __amdgpu_buffer_rsrc_t v_rsrc = byte_range(v_user + tile_off, left);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int slot = (wave * LOADS + i) * 64 + lane;
-      const int row = slot / CH, p = slot % CH;
-      const int c = p ^ swz<CH>(row);
-      const int e = um.kv_begin + min(t * BN + row, n_kv - 1);   // clamp the tail into the list
-      const int64_t g = static_cast<int64_t>(INDEXED ? a.idx[e] : e) * rs + c * 8;
-      const int lds_off = (wave * LOADS + i) * 64 * 8;           // elements; one load = 1 KiB
-      __builtin_amdgcn_global_load_lds(Kp + g, (LDS_AS void*)(dk + lds_off), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vp + g, (LDS_AS void*)(dv + lds_off), 16, 0, 0);
+      for (int i = 0; i < LOADS; ++i) {
+        const int lds_off = (wave * LOADS + i) * 64 * 8;         // elements; one load = 1 KiB
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (LDS_AS void*)(dk + lds_off), 16,
+                                                 static_cast<int>(ld_off[i]), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (LDS_AS void*)(dv + lds_off), 16,
+                                                 static_cast<int>(ld_off[i]), 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int lds_off = (wave * LOADS + i) * 64 * 8;
+        const int row = ld_row[i];
+        const int e = um.kv_begin + min(t * BN + row, n_kv - 1);   // clamp the tail into the list
+        const int64_t g = static_cast<int64_t>(INDEXED ? a.idx[e] : e) * rs * 2 +
+                          (ld_off[i] - static_cast<uint32_t>(row * rs * 2));
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(Kp) + g,
+                                         (LDS_AS void*)(dk + lds_off), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(Vp) + g,
+                                         (LDS_AS void*)(dv + lds_off), 16, 0, 0);
+      }
     }
   };
 
@@ -157,37 +221,40 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
 
-  // per-lane parts of the K operand addresses (rows kb*32 + ql)
-  int k_row_off[KB], k_mask[KB];
+  // per-lane byte offsets of the LDS operand reads (k-step / block add constants)
+  uint32_t k_off[KK];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int row = kb * 32 + ql;
-    k_row_off[kb] = row * CH;
-    k_mask[kb] = swz<CH>(row) ^ half;
+  for (int kk = 0; kk < KK; ++kk) k_off[kk] = (ql * CH + ((2 * kk + half) ^ swz<CH>(ql))) * 16;
+  uint32_t v_off[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    v_off[db][0] = vt_offset<D>(db, 0, lane);
+    v_off[db][1] = vt_offset<D>(db, 1, lane);
   }
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, auto buf_tag, auto tail_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool TAIL = decltype(tail_tag)::value;
     // tile t has landed (this wave's loads) and is visible (every wave's, after the
-    // barrier); the barrier also tells that every wave is done with buffer (t+1)&1
+    // barrier); the barrier also tells that every wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 1 < ntiles) issue_tile(t + 1);   // overlaps this tile's math
-    const u16* sk = s_k + (t & 1) * TILE;
-    const u16* sv = s_v + (t & 1) * TILE;
+    const char* sk = reinterpret_cast<const char*>(s_k + BUF * TILE);
+    const char* sv = reinterpret_cast<const char*>(s_v + BUF * TILE);
 
-    // S^T = K Q^T for this wave's 32 queries
+    // S^T = K Q^T for this wave's 32 queries; the KB accumulator chains interleave
     f32x16 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int p = (2 * kk) ^ k_mask[kb];
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + (k_row_off[kb] + p) * 8);
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + k_off[kk] + kb * 32 * CH * 16);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
       }
-    }
-    if (t == ntiles - 1 && (n_kv % BN) != 0) {
+    if constexpr (TAIL) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -196,25 +263,28 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
           if (j >= n_kv) sacc[kb][r] = -INFINITY;
         }
     }
-    // online softmax, one query per lane (key halves split across the lane halves);
-    // max and sum as trees to keep the dependency chains short
+    // online softmax, one query per lane (key halves split across the lane halves)
     float mx[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      float m4[4];
+      float m = max3f(sacc[kb][0], sacc[kb][1], sacc[kb][2]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        m4[g] = fmaxf(fmaxf(sacc[kb][4 * g], sacc[kb][4 * g + 1]),
-                      fmaxf(sacc[kb][4 * g + 2], sacc[kb][4 * g + 3]));
-      mx[kb] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      for (int r = 3; r < 15; r += 2) m = max3f(m, sacc[kb][r], sacc[kb][r + 1]);
+      mx[kb] = fmaxf(m, sacc[kb][15]);
     }
 #pragma unroll
     for (int w = 1; w < KB; w <<= 1)
 #pragma unroll
       for (int kb = 0; kb + w < KB; kb += 2 * w) mx[kb] = fmaxf(mx[kb], mx[kb + w]);
-    float tmax = fmaxf(mx[0], __shfl_xor(mx[0], 32));
-    const float m_new = fmaxf(m_i, tmax * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+    const float tmax = fmaxf(mx[0], __shfl_xor(mx[0], 32)) * sl2;
+    const bool move = tmax > m_i + kLazyRescale;   // per row: move the reference up
+    if (__any(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_i - tmax) : 1.f;
+      l_i *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_i = move ? tmax : m_i;
+    }
     float ls[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -223,7 +293,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
       for (int g = 0; g < 4; ++g) {
 #pragma unroll
         for (int r = 4 * g; r < 4 * g + 4; ++r)
-          sacc[kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m_new));
+          sacc[kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m_i));
         s4[g] = (sacc[kb][4 * g] + sacc[kb][4 * g + 1]) + (sacc[kb][4 * g + 2] + sacc[kb][4 * g + 3]);
       }
       ls[kb] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
@@ -232,12 +302,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
     for (int w = 1; w < KB; w <<= 1)
 #pragma unroll
       for (int kb = 0; kb + w < KB; kb += 2 * w) ls[kb] += ls[kb + w];
-    l_i = l_i * alpha + ls[0];
-    m_i = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
+    l_i += ls[0];
     // O^T += V^T P^T
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
@@ -246,10 +311,28 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(sacc[kb][s8 + j]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_vt<D>(sv, ks, db, lane), pf, oacc[db],
-                                                           0, 0, 0);
+      for (int db = 0; db < DB; ++db) {
+        const char* base = sv + ks * 16 * CH * 16;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_vt(base, v_off[db][0], v_off[db][1]),
+                                                           pf, oacc[db], 0, 0, 0);
+      }
     }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int full_tiles = (n_kv % BN) ? ntiles - 1 : ntiles;
+  int t = 0;
+  for (; t + 1 < full_tiles; t += 2) {
+    tile(t, B0{}, std::false_type{});
+    tile(t + 1, B1{}, std::false_type{});
+  }
+  if (t < full_tiles) {          // an odd number of full tiles: the last one is even
+    tile(t, B0{}, std::false_type{});
+    ++t;
+  }
+  if (t < ntiles) {              // the partial tail tile
+    if (t & 1) tile(t, B1{}, std::true_type{});
+    else tile(t, B0{}, std::true_type{});
   }
 
   // both lane halves hold partial sums of the same query
@@ -298,8 +381,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
         *reinterpret_cast<uint2*>(Op + qrow * rs + db * 32 + 8 * g + 4 * half) = w;
       }
   }
-  // no wave may leave while others still read LDS tiles it helped load (the loads
-  // are complete once every wave passed the last in-loop barrier), nothing to wait for
 }
 
 template <int D, int BN>

@@ -174,12 +174,19 @@ def test_history_and_cross_user_bit_identical():
     assert np.array_equal(got[s012], base[s012]), "users 0-2 depend on user 3"
 
 
-def test_deterministic_repeat():
-    fb = W.config3()
-    d = full_dev(fb)
-    a = run_full(fb, d)
+@pytest.mark.parametrize("d", [64, 128])
+def test_deterministic_repeat(d):
+    """Run-to-run bit identity (scores may be cached; a hazard or race shows up here)."""
+    fb = _property_batch(d=d)
+    dev = full_dev(fb)
+    a = run_full(fb, dev)
+    for i in range(7):
+        assert np.array_equal(run_full(fb, dev), a), f"run {i + 1} differs"
+    fb3 = W.config3()
+    dev3 = full_dev(fb3)
+    a3 = run_full(fb3, dev3)
     for _ in range(2):
-        assert np.array_equal(run_full(fb, d), a)
+        assert np.array_equal(run_full(fb3, dev3), a3)
 
 
 @pytest.mark.parametrize("d", [64, 128])
