@@ -41,7 +41,24 @@ def parse_args():
                         "6 skew padded (attend_padded_history=True), 7 skew padded (False)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="instead of the benchmark, run three plain device copies of this many MiB "
+                        "from a cold 4x larger source (reference for FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain copy kernel of known size, for scaling the HBM traffic counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(4 * n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(3):
+        dst.copy_(src[i * n:(i + 1) * n])   # a different, cold slice each time
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_per_copy": n, "copies": 3}), flush=True)
 
 
 def make_batch(cfg):
@@ -191,6 +208,9 @@ def main():
     import torch
     from jagged_candidate_isolated_amd import rr
 
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
     cfg = args.config
     b = make_batch(cfg)
     eff_flops, exec_flops, alg_bytes, n_cands = work_counts(cfg, b)
@@ -239,17 +259,34 @@ def main():
     ms_per_step = wall / steps * 1e3
     value = eff_flops / (ms_per_step / 1e3) / 1e12
 
-    # The attention kernel alone: HIP events around each launch, on the launch stream.
+    # The attention kernel alone: back-to-back launches replayed from a captured graph
+    # (no host gaps), bracketed by HIP events recorded on the launch stream.
     stream = torch.cuda.current_stream()
-    n_ev = max(20, min(steps, 400))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
     plan()
-    for i in range(n_ev):
-        ev[i][0].record(stream)
-        run(i)
-        ev[i][1].record(stream)
+    n_run = copies
+    run_graph = None
+    try:
+        run_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(run_graph):
+            for i in range(n_run):
+                run(i)
+        run_graph.replay()
+    except Exception as e:  # pragma: no cover
+        print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
+        run_graph = None
     torch.cuda.synchronize()
-    kernel_ms = float(np.median([a.elapsed_time(c) for a, c in ev]))
+    reps_k = max(2, math.ceil(max(20, min(steps, 400)) / n_run))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps_k):
+        if run_graph is not None:
+            run_graph.replay()
+        else:
+            for i in range(n_run):
+                run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = e0.elapsed_time(e1) / (reps_k * n_run)
 
     flop_per_byte = eff_flops / alg_bytes
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
