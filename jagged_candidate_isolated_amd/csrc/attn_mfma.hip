@@ -383,12 +383,24 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   }
 }
 
+// XCD-aware item order.  Workgroup i runs on XCD i % kXcds (the dispatcher deals
+// workgroups out round-robin), each XCD with its own L2.  Chunks of kXcdChunk
+// consecutive items -- query tiles of one user and head, which read the same keys
+// and values -- go to one XCD together, chunk c to XCD c % kXcds, so a K/V tile
+// comes into that L2 once and serves the whole chunk; chunks still start in the
+// work list's longest-first order.  The grid is a multiple of kXcds * kXcdChunk,
+// which makes the map a permutation.
+__device__ __forceinline__ int xcd_item(int wg) {
+  const int x = wg % kXcds, slot = wg / kXcds;
+  return ((slot / kXcdChunk) * kXcds + x) * kXcdChunk + slot % kXcdChunk;
+}
+
 template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) u16 s_k[2 * BN * D];   // double-buffered K tiles
   __shared__ __attribute__((aligned(16))) u16 s_v[2 * BN * D];   // double-buffered V tiles
   if (!plan_matches(a, kBm)) return;
-  const int item = blockIdx.x;
+  const int item = xcd_item(blockIdx.x);
   if (item >= a.plan->n_items) return;
   const int2 it = a.items[item];
   if (item_head(it) == kZeroHead) {

@@ -65,15 +65,24 @@ struct WsLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workgroups of an attention launch for tile height bm: one per possible work item.
+// XCDs of an MI355X and the number of consecutive work items the MFMA kernel keeps
+// together on one XCD (for L2 reuse of a user's keys and values).
+constexpr int kXcds = 8;
+constexpr int kXcdChunk = 8;
+
+// Workgroups of an attention launch for tile height bm: one per possible work item,
+// rounded up to whole XCD chunks.
 inline int64_t attn_grid(int64_t B, int64_t rows, int64_t H, int bm) {
-  return (H + 1) * ((rows + bm - 1) / bm + B);
+  const int64_t n = (H + 1) * ((rows + bm - 1) / bm + B);
+  const int64_t q = int64_t(kXcds) * kXcdChunk;
+  return (n + q - 1) / q * q;
 }
 
 inline int64_t item_upper_bound(int64_t B, int64_t rows, int64_t H) {
   // sum_b ceil(n_b / BM) <= rows / BM + B for any split of `rows` over B users;
   // H attention items per query tile plus at most one zeroing item per padding tile
-  return (H + 1) * ((rows + kBmMin - 1) / kBmMin + B);
+  // (>= attn_grid for every tile height, so the items array holds any capped list)
+  return attn_grid(B, rows, H, kBmMin);
 }
 
 inline WsLayout ws_layout(int64_t B, int64_t T_idx, int64_t q_rows, int64_t H) {
