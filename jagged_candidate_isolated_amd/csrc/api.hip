@@ -14,8 +14,13 @@ bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 int status_of(hipError_t e) { return e == hipSuccess ? RR_OK : RR_EHIP; }
 
 // The MFMA kernel takes bf16 with d >= 32; everything else runs on the VALU kernel.
+// Its wide tile (256 query rows, deeper pipeline) pays off when users are long; the
+// choice depends on host-known sizes only, so a plan and its run always agree.
 bool use_mfma(int dtype, int d) { return dtype == RR_BF16 && d >= 32; }
-int tile_rows(int dtype, int d) { return use_mfma(dtype, d) ? kBmMfma : kBmSimple; }
+int tile_rows(int dtype, int d, int64_t B, int64_t rows) {
+  if (!use_mfma(dtype, d)) return kBmSimple;
+  return rows >= int64_t(kWideMinRows) * B ? kBmMfmaWide : kBmMfmaNarrow;
+}
 
 float softmax_scale_log2(float scale, int d) {
   const float s = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf(static_cast<float>(d));
@@ -52,7 +57,7 @@ Ws carve_all(void* ws, const WsLayout& w) {
 
 int run_attention(const AttnArgs& a, int dtype, int d, int bm, int64_t rows, hipStream_t stream) {
   const int64_t grid = attn_grid(a.B, rows, a.H, bm);
-  const hipError_t e = use_mfma(dtype, d) ? launch_attn_mfma(a, d, grid, stream)
+  const hipError_t e = use_mfma(dtype, d) ? launch_attn_mfma(a, d, bm, grid, stream)
                                           : launch_attn_simple(a, d, dtype, grid, stream);
   return status_of(e);
 }
@@ -108,7 +113,7 @@ int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_
   const WsLayout w = ws_layout(B, T, T, H);
   if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
   const Ws p = carve_all(workspace, w);
-  const int bm = tile_rows(dtype, d);
+  const int bm = tile_rows(dtype, d, B, T);
   const int64_t cap = attn_grid(B, T, H, bm);   // <= w.item_bound
   hipError_t e = hipSuccess;
   if (valid) {
@@ -141,7 +146,7 @@ int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B,
   a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
   a.B = B; a.H = H; a.mode = 0; a.rows = T;
   a.scale_log2 = softmax_scale_log2(scale, d);
-  return run_attention(a, dtype, d, tile_rows(dtype, d), T, stream);
+  return run_attention(a, dtype, d, tile_rows(dtype, d, B, T), T, stream);
 }
 
 int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
@@ -173,7 +178,7 @@ int rr_cand_only_plan(const int32_t* hist_offsets, const int32_t* cand_offsets, 
   const WsLayout w = ws_layout(B, 0, Tc, H);
   if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
   const Ws p = carve_all(workspace, w);
-  const int bm = tile_rows(dtype, d);
+  const int bm = tile_rows(dtype, d, B, Tc);
   const int64_t cap = attn_grid(B, Tc, H, bm);   // <= w.item_bound
   return status_of(launch_worklist(1, hist_offsets, cand_offsets, 0, B, H, bm, Tc, Th,
                                    static_cast<int>(cap), p.meta, p.start, p.items, p.header, stream));
@@ -199,7 +204,7 @@ int rr_cand_only_run(const void* q_cand, const void* k_hist, const void* v_hist,
   a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
   a.B = B; a.H = H; a.mode = 1; a.rows = Tc;
   a.scale_log2 = softmax_scale_log2(scale, d);
-  return run_attention(a, dtype, d, tile_rows(dtype, d), Tc, stream);
+  return run_attention(a, dtype, d, tile_rows(dtype, d, B, Tc), Tc, stream);
 }
 
 int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_hist,

@@ -1,15 +1,15 @@
 // bf16 attention kernel on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Work item = (user, head, 128-query tile); a workgroup of four waves, 32 query
-// rows per wave.  Under the candidate-isolation mask (Candidate isolation
+// Work item = (user, head, query tile of NW*32 rows); a workgroup of NW waves, 32
+// query rows per wave.  Under the candidate-isolation mask (Candidate isolation
 // attention mask page, section "段 ID：掩码的表达方式") every valid query of a user
 // reads the same key list -- the user's segment-1 rows, or in a candidate-only
 // layer the frozen history (section "只更新候选的末尾层") -- so the main loop is a
-// dense, unmasked rectangle: each K/V tile is staged once in LDS and shared by
-// all 128 queries of the tile, history rows and candidates alike.  Only the last
-// key tile is masked (its tail past the key count).  A candidate's extra key,
-// itself, is added after the loop as a dot product across the wave's two lane
-// halves rather than as a masked tile.
+// dense, unmasked rectangle: each K/V tile is staged once in LDS and shared by all
+// queries of the tile, history rows and candidates alike.  Only the last key tile
+// is masked (its tail past the key count).  A candidate's extra key, itself, is
+// added after the loop as a dot product across the wave's two lane halves rather
+// than as a masked tile.
 //
 // Matrix orientation.  The kernel computes S^T = K Q^T so that each lane owns one
 // query column of the 32x32 accumulator: the softmax row statistics (max, sum)
@@ -21,113 +21,35 @@
 //   B operand (16 x 32): column i, k = 8*half + j
 //   C/D (32 x 32, 16 fp32): column i, row 8*(r/4) + 4*half + r%4   (r = 0..15)
 // P^T's k index therefore comes out of the accumulator in a permuted key order
-// (bits 2 and 3 of the key index within each group of 16 swapped); V^T is written
-// to LDS in that same permuted order so the A and B operands agree.
+// (bits 2 and 3 of the key index within each group of 16 swapped); the V^T
+// operand is read in that same permuted order so the A and B operands agree.
+//
+// Pipeline.  K and V tiles go to LDS by direct-to-LDS loads (no register staging)
+// into NS rotating buffers, NS-1 tiles ahead of the tile being computed; one
+// barrier per tile.  This kernel takes the short users (four waves, 128 query rows,
+// two stages, two workgroups per CU); long users go to the two-block kernel in
+// attn_pp.hip.
 //
 // Numerics: bf16 operands, fp32 accumulation, online softmax in fp32 with exp2
 // (scale * log2 e folded into one FMA), P rounded to bf16 for the PV product,
 // output rounded to bf16 (round to nearest even).
-#include <type_traits>
-
-#include "rr_internal.h"
+#include "mfma_tile.h"
 
 namespace rr {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned short u16;
-
-constexpr int kWaves = 4;
-constexpr int kQw = 32;                  // query rows per wave
-constexpr int kBm = kWaves * kQw;        // query rows per work item
-static_assert(kBm == kBmMfma, "tile height");
-constexpr int kThreads = kWaves * 64;
-
-__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-  return __builtin_bit_cast(unsigned, v);
-}
-
-// LDS tile layout.  A K or V tile is BN rows of D bf16 (row-major), stored in
-// 16-byte chunks; chunk c of row r sits at position c ^ swz(r) of that row.  The
-// swizzle keeps both kinds of reads free of bank conflicts: the K reads (16
-// consecutive rows, one chunk each) and the transposed V reads (4 consecutive rows,
-// 4 chunks each) touch distinct banks.  Tiles arrive by direct-to-LDS loads: lane l
-// of a load writes LDS slot l, so the swizzle is applied by choosing which global
-// chunk each lane fetches.
-template <int CH>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (CH == 16) return 4 * (row & 3) + ((row >> 2) & 3);
-  else if constexpr (CH == 8) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
-  else return (row >> 2) & 3;   // CH == 4: 64-byte rows
-}
-
-#define LDS_AS __attribute__((address_space(3)))
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// V^T operand of the PV product: eight keys of one V column per lane, read with two
-// transposed LDS loads.  Within each 16-lane group the transposed load returns, in
-// lane j, element j%4 of the 8-byte pieces addressed by lanes 4k + j/4 (k = 0..3); so
-// lane s of a group addresses row (key) 4*half + s/4 at columns 4*(s%4)..+3 of the
-// group's 16 columns, and receives one column, four keys.  vt_offset() gives the
-// byte offset of that piece for k-step 0; k-step ks adds ks * 16 rows.
-template <int D>
-__device__ __forceinline__ uint32_t vt_offset(int db, int part, int lane) {
-  constexpr int CH = D / 8;
-  const int s = lane & 15, grp = (lane >> 4) & 1, half = lane >> 5;
-  const int col = db * 32 + 16 * grp + 4 * (s & 3);      // first of 4 columns (elements)
-  const int c = col >> 3, sub = (col & 7) * 2;           // 16-byte chunk, byte offset in it
-  const int row = 8 * part + 4 * half + (s >> 2);        // swz() ignores multiples of 16 rows
-  return static_cast<uint32_t>((row * CH + (c ^ swz<CH>(row))) * 16 + sub);
-}
-
-__device__ __forceinline__ bf16x8 read_vt(const char* sv, uint32_t off0, uint32_t off1) {
-  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(sv + off0));
-  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(sv + off1));
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 w = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-// Max of three.  This file is compiled without NaN support (no value here is ever
-// NaN: scores are finite or -inf, and no expression subtracts two infinities), so
-// the compiler emits v_max3_f32 directly instead of first canonicalising each MFMA
-// result for IEEE maxNum semantics.
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
-
-// Buffer resource of a raw byte range (gfx9 dword 3: 32-bit data, no swizzle); loads
-// past `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
-}
-
-// Rows keep their running maximum as the softmax reference until a tile's maximum
-// exceeds it by more than 2^kLazyRescale (log2 units); only then are the row's
-// accumulator and sum rescaled.  Probabilities stay below 2^kLazyRescale, far from
-// any overflow, and each row decides for itself, so a row's result never depends
-// on the other rows of its wave.
-#ifndef RR_LAZY_RESCALE
-#define RR_LAZY_RESCALE 8.f
-#endif
-constexpr float kLazyRescale = RR_LAZY_RESCALE;
-
-template <int D, int BN, bool INDEXED>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16* __restrict__ s_k,
-                                          u16* __restrict__ s_v) {
+template <int D, int BN, int NW, int NS, bool KEY_IDX>
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, const Stages& st) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kBm = NW * kQw;
+  using Loader = KvLoader<D, BN, kThreads, KEY_IDX>;
   constexpr int CH = D / 8;                  // 16-byte chunks per row
-  constexpr int TILE = BN * D;               // elements per K (or V) tile
-  constexpr int LOADS = TILE * 2 / (kThreads * 16);   // direct-to-LDS loads per thread per tile
+  constexpr int LPT = Loader::LPT;           // vector-memory operations per thread per tile
   constexpr int KK = D / 16;                 // k-steps of S^T
   constexpr int KB = BN / 32;                // 32-key blocks per tile
   constexpr int DB = D / 32;                 // 32-wide blocks of O^T
-  static_assert(D % 32 == 0 && BN % 32 == 0 && LOADS >= 1 && TILE * 2 % (kThreads * 16) == 0,
-                "tile shape");
+  static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(NS >= 2 && NS <= 4, "pipeline stages");
 
   const int b = it.x, h = item_head(it), qt = item_tile(it);
   const UserMeta um = a.meta[b];
@@ -143,83 +65,48 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   u16* __restrict__ Op = static_cast<u16*>(a.o) + h * D;
   const float sl2 = a.scale_log2;
 
-  // this lane's query row
+  // this lane's query row, and its Q operand (loaded before any tile, so the tile
+  // loads are the only vector-memory operations the loop waits on)
   const int qpos = qt * kBm + wave * kQw + ql;
   const bool qvalid = qpos < um.n_q;
   const int qe = um.q_begin + min(qpos, um.n_q - 1);
-  const int qrow = INDEXED ? a.idx[qe] : qe;
-
-  const int n_kv = um.n_kv;
-  const int ntiles = (n_kv + BN - 1) / BN;
-
-  // Direct-to-LDS loads of key/value tile t into buffer t & 1.  Load i of wave w fills
-  // LDS slots (w*LOADS + i)*64 + lane; slot -> (row, chunk position) -> global chunk.
-  // A full tile of a plain row list is one byte range: a buffer resource whose per-lane
-  // offsets never change between tiles.  The partial last tile, and row lists through
-  // idx[], load per row with the row index clamped into the key list (the last tile
-  // masks the repeated rows), so every byte that reaches LDS is a real key or value.
-  int ld_row[LOADS];
-  uint32_t ld_off[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int slot = (wave * LOADS + i) * 64 + lane;
-    const int row = slot / CH, p = slot % CH;
-    ld_row[i] = row;
-    ld_off[i] = static_cast<uint32_t>(row * rs * 2 + (p ^ swz<CH>(row)) * 16);
-  }
-  const int64_t user_bytes = n_kv > 0 ? (static_cast<int64_t>(n_kv - 1) * rs + D) * 2 : 0;
-#ifdef RR_NO_RANGED_LOADS
-  const bool ranged = false;
-#else
-  const bool ranged = !INDEXED && user_bytes + static_cast<int64_t>(BN) * rs * 2 < (int64_t(1) << 31);
-#endif
-  const char* k_user = reinterpret_cast<const char*>(Kp) + static_cast<int64_t>(um.kv_begin) * rs * 2;
-  const char* v_user = reinterpret_cast<const char*>(Vp) + static_cast<int64_t>(um.kv_begin) * rs * 2;
-  auto issue_tile = [&](int t) {
-    u16* dk = s_k + (t & 1) * TILE;
-    u16* dv = s_v + (t & 1) * TILE;
-    if (ranged && (t + 1) * BN <= n_kv) {
-      // a full tile: the descriptor starts at the tile and ends at the user's last key
-      // byte, so the range check also keeps every load inside the user's keys
-      const int64_t tile_off = static_cast<int64_t>(t) * BN * rs * 2;
-      const uint32_t left = static_cast<uint32_t>(user_bytes - tile_off);
-      const __amdgpu_buffer_rsrc_t k_rsrc = byte_range(k_user + tile_off, left);
-      const __amdgpu_buffer_rsrc_t v_rsrc = byte_range(v_user + tile_off, left);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int lds_off = (wave * LOADS + i) * 64 * 8;         // elements; one load = 1 KiB
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (LDS_AS void*)(dk + lds_off), 16,
-                                                 static_cast<int>(ld_off[i]), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (LDS_AS void*)(dv + lds_off), 16,
-                                                 static_cast<int>(ld_off[i]), 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int lds_off = (wave * LOADS + i) * 64 * 8;
-        const int row = ld_row[i];
-        const int e = um.kv_begin + min(t * BN + row, n_kv - 1);   // clamp the tail into the list
-        const int64_t g = static_cast<int64_t>(INDEXED ? a.idx[e] : e) * rs * 2 +
-                          (ld_off[i] - static_cast<uint32_t>(row * rs * 2));
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(Kp) + g,
-                                         (LDS_AS void*)(dk + lds_off), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(Vp) + g,
-                                         (LDS_AS void*)(dv + lds_off), 16, 0, 0);
-      }
-    }
-  };
-
-  if (ntiles > 0) issue_tile(0);
-
+  const int qrow = a.plan->indexed ? a.idx[qe] : qe;
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(Qp + qrow * rs + 16 * kk + 8 * half);
 
+  const int n_kv = um.n_kv;
+  const int ntiles = (n_kv + BN - 1) / BN;
+
+  constexpr int AHEAD = NS - 1;   // tiles loaded ahead of the tile being computed
+  static_assert((AHEAD - 1) * Loader::LPT < 64, "pipeline depth");
+
+  // direct-to-LDS loads of key/value tile t into stage t % NS
+  const Loader ld(Kp, Vp, a.idx, rs, um.kv_begin, n_kv, tid);
+  auto issue_tile = [&](int t, auto stage_tag) {
+    constexpr int STAGE = decltype(stage_tag)::value;
+    ld.issue(t, st.k[STAGE], st.v[STAGE]);
+  };
+
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1 % NS>;
+  using C2 = std::integral_constant<int, 2 % NS>;
+  using C3 = std::integral_constant<int, 3 % NS>;
+  // prologue: the first AHEAD tiles in flight
+  if (0 < ntiles) issue_tile(0, C0{});
+  if constexpr (AHEAD > 1) {
+    if (1 < ntiles) issue_tile(1, C1{});
+  }
+  if constexpr (AHEAD > 2) {
+    if (2 < ntiles) issue_tile(2, C2{});
+  }
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
+  f32x16 sacc[KB];   // S^T of the tile between its S and PV steps (P after the softmax)
 
   // per-lane byte offsets of the LDS operand reads (k-step / block add constants)
   uint32_t k_off[KK];
@@ -232,19 +119,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
     v_off[db][1] = vt_offset<D>(db, 1, lane);
   }
 
-  auto tile = [&](int t, auto buf_tag, auto tail_tag) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    // tile t has landed (this wave's loads) and is visible (every wave's, after the
-    // barrier); the barrier also tells that every wave is done with the other buffer
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1);   // overlaps this tile's math
-    const char* sk = reinterpret_cast<const char*>(s_k + BUF * TILE);
-    const char* sv = reinterpret_cast<const char*>(s_v + BUF * TILE);
-
-    // S^T = K Q^T for this wave's 32 queries; the KB accumulator chains interleave
-    f32x16 sacc[KB];
+  // S^T = K Q^T for this wave's 32 queries; the KB accumulator chains interleave
+  auto s_step = [&](auto stage_tag) {
+    const char* sk = reinterpret_cast<const char*>(st.k[decltype(stage_tag)::value]);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
@@ -254,16 +131,24 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + k_off[kk] + kb * 32 * CH * 16);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
       }
-    if constexpr (TAIL) {
+  };
+  // online softmax of tile t, one query per lane (key halves split across the lane halves)
+  auto softmax_step = [&](int t) {
+    if ((t + 1) * BN > n_kv) {
+      // The partial last tile: keys past the list get -inf.  Element (kb, r) of this
+      // lane is key t*BN + c + 4*half with c = 32 kb + 8 (r/4) + r%4; it is masked
+      // when c >= lim.  Adding 0 or -inf built from the sign of c - lim keeps the
+      // per-element tests in vector registers (compares would each take a scalar
+      // lane mask).
+      const int lim = n_kv - t * BN - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = t * BN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (j >= n_kv) sacc[kb][r] = -INFINITY;
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          sacc[kb][r] += __int_as_float(~((c - lim) >> 31) & static_cast<int>(0xff800000u));
         }
     }
-    // online softmax, one query per lane (key halves split across the lane halves)
     float mx[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -276,7 +161,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
     for (int w = 1; w < KB; w <<= 1)
 #pragma unroll
       for (int kb = 0; kb + w < KB; kb += 2 * w) mx[kb] = fmaxf(mx[kb], mx[kb + w]);
-    const float tmax = fmaxf(mx[0], __shfl_xor(mx[0], 32)) * sl2;
+    const float tmax = halves_max(mx[0]) * sl2;
     const bool move = tmax > m_i + kLazyRescale;   // per row: move the reference up
     if (__any(move)) {
       const float alpha = move ? __builtin_amdgcn_exp2f(m_i - tmax) : 1.f;
@@ -303,7 +188,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
 #pragma unroll
       for (int kb = 0; kb + w < KB; kb += 2 * w) ls[kb] += ls[kb + w];
     l_i += ls[0];
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T
+  auto pv_step = [&](auto stage_tag) {
+    const char* sv = reinterpret_cast<const char*>(st.v[decltype(stage_tag)::value]);
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
       const int kb = ks >> 1, s8 = (ks & 1) * 8;
@@ -318,25 +206,34 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
       }
     }
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  const int full_tiles = (n_kv % BN) ? ntiles - 1 : ntiles;
-  int t = 0;
-  for (; t + 1 < full_tiles; t += 2) {
-    tile(t, B0{}, std::false_type{});
-    tile(t + 1, B1{}, std::false_type{});
-  }
-  if (t < full_tiles) {          // an odd number of full tiles: the last one is even
-    tile(t, B0{}, std::false_type{});
-    ++t;
-  }
-  if (t < ntiles) {              // the partial tail tile
-    if (t & 1) tile(t, B1{}, std::true_type{});
-    else tile(t, B0{}, std::true_type{});
-  }
 
+  auto tile = [&](int t, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    // Tile t has landed once no more than the loads of the tiles issued after it are
+    // outstanding (this wave's loads, retiring in order); the barrier makes every
+    // wave's loads visible and tells that every wave is done with the stage of tile
+    // t+AHEAD, refilled next to overlap the following tiles' math.
+    wait_tiles<LPT>(min(AHEAD - 1, ntiles - 1 - t));
+    tile_barrier();
+    if (t + AHEAD < ntiles) issue_tile(t + AHEAD, std::integral_constant<int, (CUR + AHEAD) % NS>{});
+    s_step(cur_tag);
+    softmax_step(t);
+    pv_step(cur_tag);
+  };
+  // One loop, NS tiles per trip, so that tile t always uses stage t % NS as a
+  // compile-time constant; the tiles past the end of the list are skipped.
+  for (int t = 0; t < ntiles; t += NS) {
+    tile(t, C0{});
+    if (t + 1 < ntiles) tile(t + 1, C1{});
+    if constexpr (NS > 2) {
+      if (t + 2 < ntiles) tile(t + 2, C2{});
+    }
+    if constexpr (NS > 3) {
+      if (t + 3 < ntiles) tile(t + 3, C3{});
+    }
+  }
   // both lane halves hold partial sums of the same query
-  float l_tot = l_i + __shfl_xor(l_i, 32);
+  float l_tot = halves_sum(l_i);
 
   // candidate self-term: <q, own k> as a dot product split across the two halves
   float sd = 0.f;
@@ -350,7 +247,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
       sd = fmaf(static_cast<float>(qf[kk][2 * j + 1]), bf16_hi(kwv[j]), sd);
     }
   }
-  sd += __shfl_xor(sd, 32);
+  sd = halves_sum(sd);
   if (qpos >= um.cand_rel) {
     const float ts = sd * sl2;
     const float mn = fmaxf(m_i, ts);
@@ -383,48 +280,70 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, u16*
   }
 }
 
-// XCD-aware item order.  Workgroup i runs on XCD i % kXcds (the dispatcher deals
-// workgroups out round-robin), each XCD with its own L2.  Chunks of kXcdChunk
-// consecutive items -- query tiles of one user and head, which read the same keys
-// and values -- go to one XCD together, chunk c to XCD c % kXcds, so a K/V tile
-// comes into that L2 once and serves the whole chunk; chunks still start in the
-// work list's longest-first order.  The grid is a multiple of kXcds * kXcdChunk,
-// which makes the map a permutation.
-__device__ __forceinline__ int xcd_item(int wg) {
-  const int x = wg % kXcds, slot = wg / kXcds;
-  return ((slot / kXcdChunk) * kXcds + x) * kXcdChunk + slot % kXcdChunk;
-}
-
-template <int D, int BN>
-__global__ __launch_bounds__(kThreads, 2) void k_attn_mfma(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 s_k[2 * BN * D];   // double-buffered K tiles
-  __shared__ __attribute__((aligned(16))) u16 s_v[2 * BN * D];   // double-buffered V tiles
-  if (!plan_matches(a, kBm)) return;
+template <int D, int BN, int NW, int NS>
+__global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
+  // pipeline stages (stages past NS are never referenced and take no LDS)
+  __shared__ __attribute__((aligned(16))) u16 k0[BN * D], k1[BN * D], k2[BN * D], k3[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 v0[BN * D], v1[BN * D], v2[BN * D], v3[BN * D];
+  const Stages st{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
+  if (!plan_matches(a, NW * kQw)) return;
   const int item = xcd_item(blockIdx.x);
   if (item >= a.plan->n_items) return;
   const int2 it = a.items[item];
   if (item_head(it) == kZeroHead) {
-    zero_padding_tile(a, a.meta[it.x], item_tile(it), kBm, a.H * D * 2, threadIdx.x, kThreads);
+    zero_padding_tile(a, a.meta[it.x], item_tile(it), NW * kQw, a.H * D * 2, threadIdx.x, NW * 64);
     return;
   }
-  if (a.plan->indexed)
-    attn_item<D, BN, true>(a, it, s_k, s_v);
+  // key rows go through idx[] only for a padded user whose key rows are not one range
+  if (a.plan->indexed && !a.meta[it.x].kv_direct)
+    attn_item<D, BN, NW, NS, true>(a, it, st);
   else
-    attn_item<D, BN, false>(a, it, s_k, s_v);
+    attn_item<D, BN, NW, NS, false>(a, it, st);
 }
 
-template <int D, int BN>
+template <int D, int BN, int NW, int NS>
 hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
-  return launch1(k_attn_mfma<D, BN>, grid, kThreads, s, a);
+  return launch1(k_attn_mfma<D, BN, NW, NS>, grid, NW * 64, s, a);
 }
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const AttnArgs& a, int d, int64_t grid, hipStream_t s) {
+// Tile shapes (compile-time tuning knobs).  Narrow: four waves, 128 query rows, two
+// workgroups per CU.  Wide: eight waves, 256 query rows, one workgroup per CU.
+#ifndef RR_NARROW_STAGES
+#define RR_NARROW_STAGES 2
+#endif
+#ifndef RR_NARROW_BN64
+#define RR_NARROW_BN64 128
+#endif
+#ifndef RR_NARROW_BN128
+#define RR_NARROW_BN128 64
+#endif
+#ifndef RR_WIDE_STAGES
+#define RR_WIDE_STAGES 4
+#endif
+#ifndef RR_WIDE_BN64
+#define RR_WIDE_BN64 128
+#endif
+#ifndef RR_WIDE_BN128
+#define RR_WIDE_BN128 64
+#endif
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s) {
+  if (bm == kBmMfmaWide) {
+    constexpr int NW = kBmMfmaWide / kQw, NS = RR_WIDE_STAGES;
+    switch (d) {
+      case 32: return go<32, 128, NW, NS>(a, grid, s);
+      case 64: return go<64, RR_WIDE_BN64, NW, NS>(a, grid, s);
+      case 128: return go<128, RR_WIDE_BN128, NW, NS>(a, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  constexpr int NW = kBmMfmaNarrow / kQw, NS = RR_NARROW_STAGES;
   switch (d) {
-    case 32: return go<32, 128>(a, grid, s);
-    case 64: return go<64, 128>(a, grid, s);
-    case 128: return go<128, 64>(a, grid, s);
+    case 32: return go<32, 128, NW, NS>(a, grid, s);
+    case 64: return go<64, RR_NARROW_BN64, NW, NS>(a, grid, s);
+    case 128: return go<128, RR_NARROW_BN128, NW, NS>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,7 +22,7 @@ __device__ __forceinline__ float ld(const __bf16* p) { return static_cast<float>
 __device__ __forceinline__ void st(float* p, float x) { *p = x; }
 __device__ __forceinline__ void st(__bf16* p, float x) { *p = static_cast<__bf16>(x); }
 
-template <typename T, int D, bool INDEXED>
+template <typename T, int D, bool KEY_IDX>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it,
                                           float (*__restrict__ s_k)[D], float (*__restrict__ s_v)[D]) {
   constexpr int kKeys = keys_per_tile<D>();
@@ -40,7 +40,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it,
   const int qpos = qt * kLanes + lane;
   const bool qvalid = qpos < um.n_q;
   const int qe = um.q_begin + min(qpos, um.n_q - 1);
-  const int qrow = INDEXED ? a.idx[qe] : qe;
+  const int qrow = a.plan->indexed ? a.idx[qe] : qe;
   const float sl2 = a.scale_log2;
 
   float q[D], acc[D];
@@ -56,7 +56,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it,
     if (lane < kKeys) {
       const int j = min(j0 + lane, n_kv - 1);
       const int ke = um.kv_begin + j;
-      const int krow = INDEXED ? a.idx[ke] : ke;
+      const int krow = KEY_IDX ? a.idx[ke] : ke;
 #pragma unroll
       for (int e = 0; e < D; ++e) {
         s_k[lane][e] = ld(K + krow * rs + h * D + e);
@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kLanes) void k_attn_simple(AttnArgs a) {
                       kLanes);
     return;
   }
-  if (a.plan->indexed)
+  // key rows go through idx[] only for a padded user whose key rows are not one range
+  if (a.plan->indexed && !a.meta[it.x].kv_direct)
     attn_item<T, D, true>(a, it, s_k, s_v);
   else
     attn_item<T, D, false>(a, it, s_k, s_v);

@@ -11,8 +11,14 @@ namespace rr {
 
 // Query-row tile heights of the attention kernels.  The work-list and the
 // workspace are sized with the smallest one.
-constexpr int kBmSimple = 64;    // fp32 (and bf16 d=16) VALU kernel: one wave, one row per lane
-constexpr int kBmMfma = 128;     // bf16 MFMA kernel: four waves of 32 query rows
+constexpr int kBmSimple = 64;      // fp32 (and bf16 d=16) VALU kernel: one wave, one row per lane
+constexpr int kBmMfmaNarrow = 128; // bf16 MFMA kernel, short users: four waves of 32 query rows
+constexpr int kBmMfmaWide = 256;   // bf16 MFMA kernel, long users: eight waves of 32 query rows
+// Average rows per user from which the wide tile is used (compile-time tuning knob).
+#ifndef RR_WIDE_MIN_ROWS
+#define RR_WIDE_MIN_ROWS 2048
+#endif
+constexpr int kWideMinRows = RR_WIDE_MIN_ROWS;
 constexpr int kBmMin = 64;
 constexpr int kHeadSlots = 1024; // work items pack the head into 10 bits ...
 constexpr int kZeroHead = 1023;  // ... and head 1023 marks "zero these padding rows"
@@ -29,7 +35,8 @@ struct UserMeta {
   int32_t n_kv;      // keys every query of the user reads (segment-1 / frozen rows)
   int32_t cand_rel;  // query-list position of the first candidate (self-term from here on)
   int32_t n_pad;     // padding rows (segment 0), listed in idx right after the query list
-  int32_t spare0, spare1;
+  int32_t kv_direct; // keys are rows kv_begin + j even in an indexed plan (one contiguous range)
+  int32_t spare1;
 };
 static_assert(sizeof(UserMeta) == 32, "UserMeta is 32 bytes");
 
@@ -68,7 +75,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // XCDs of an MI355X and the number of consecutive work items the MFMA kernel keeps
 // together on one XCD (for L2 reuse of a user's keys and values).
 constexpr int kXcds = 8;
-constexpr int kXcdChunk = 8;
+#ifndef RR_XCD_CHUNK
+#define RR_XCD_CHUNK 8
+#endif
+constexpr int kXcdChunk = RR_XCD_CHUNK;
 
 // Workgroups of an attention launch for tile height bm: one per possible work item,
 // rounded up to whole XCD chunks.
@@ -159,14 +169,14 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
                            int B, int H, int bm, int rows, int kv_rows, int cap, UserMeta* meta,
                            int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
-hipError_t launch_attn_mfma(const AttnArgs& a, int d, int64_t grid, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
 
 // Zero the output rows of a padding tile: rows idx[q_begin + n_q + qt*bm ...], every head.
 // `nthreads` threads of the workgroup cooperate; rows are `row_bytes` long (a multiple of 16).
 __device__ __forceinline__ void zero_padding_tile(const AttnArgs& a, const UserMeta& um, int qt,
                                                   int bm, int row_bytes, int tid, int nthreads) {
   const int first = qt * bm;
-  const int nrows = min(bm, um.n_pad - first);
+  const int nrows = min(bm, um.n_pad - first);   // padding rows follow the query list in idx
   const int chunks = row_bytes / 16;
   uint4* o = static_cast<uint4*>(a.o);
   for (int e = tid; e < nrows * chunks; e += nthreads) {

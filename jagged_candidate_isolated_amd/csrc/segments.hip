@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
       n_hist += tot_h;
       n_pad += tot_p;
     }
+    __syncthreads();   // this workgroup's idx writes are visible to its threads
     if (threadIdx.x == 0) {
       UserMeta m{};
       m.q_begin = lo;
@@ -167,6 +168,14 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
       m.n_kv = n_hist;
       m.cand_rel = n_hist;
       m.n_pad = n_pad;
+      // keys that form one row range (e.g. padding attended as history) load directly
+      if (n_hist > 0) {
+        const int first = p.idx[lo], last = p.idx[lo + n_hist - 1];
+        if (last - first + 1 == n_hist) {
+          m.kv_direct = 1;
+          m.kv_begin = first;
+        }
+      }
       p.meta[b] = m;
     }
   }
