@@ -39,7 +39,8 @@ namespace rr {
 namespace {
 
 template <int D, int BN, int NW, int NS, bool KEY_IDX>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, const Stages& st) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, const UserMeta& um,
+                                          bool indexed, const Stages& st) {
   constexpr int kThreads = NW * 64;
   constexpr int kBm = NW * kQw;
   using Loader = KvLoader<D, BN, kThreads, KEY_IDX>;
@@ -51,8 +52,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
   static_assert(NS >= 2 && NS <= 4, "pipeline stages");
 
-  const int b = it.x, h = item_head(it), qt = item_tile(it);
-  const UserMeta um = a.meta[b];
+  const int h = item_head(it), qt = item_tile(it);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, ql = lane & 31;
@@ -70,7 +70,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   const int qpos = qt * kBm + wave * kQw + ql;
   const bool qvalid = qpos < um.n_q;
   const int qe = um.q_begin + min(qpos, um.n_q - 1);
-  const int qrow = a.plan->indexed ? a.idx[qe] : qe;
+  const int qrow = indexed ? a.idx[qe] : qe;
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
@@ -286,19 +286,19 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) u16 k0[BN * D], k1[BN * D], k2[BN * D], k3[BN * D];
   __shared__ __attribute__((aligned(16))) u16 v0[BN * D], v1[BN * D], v2[BN * D], v3[BN * D];
   const Stages st{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
-  if (!plan_matches(a, NW * kQw)) return;
-  const int item = xcd_item(blockIdx.x);
-  if (item >= a.plan->n_items) return;
-  const int2 it = a.items[item];
+  int2 it;
+  UserMeta um;
+  bool indexed;
+  if (!fetch_item(a, NW * kQw, xcd_item(blockIdx.x), it, um, indexed)) return;
   if (item_head(it) == kZeroHead) {
-    zero_padding_tile(a, a.meta[it.x], item_tile(it), NW * kQw, a.H * D * 2, threadIdx.x, NW * 64);
+    zero_padding_tile(a, um, item_tile(it), NW * kQw, a.H * D * 2, threadIdx.x, NW * 64);
     return;
   }
   // key rows go through idx[] only for a padded user whose key rows are not one range
-  if (a.plan->indexed && !a.meta[it.x].kv_direct)
-    attn_item<D, BN, NW, NS, true>(a, it, st);
+  if (indexed && !um.kv_direct)
+    attn_item<D, BN, NW, NS, true>(a, it, um, indexed, st);
   else
-    attn_item<D, BN, NW, NS, false>(a, it, st);
+    attn_item<D, BN, NW, NS, false>(a, it, um, indexed, st);
 }
 
 template <int D, int BN, int NW, int NS>

@@ -23,11 +23,11 @@ __device__ __forceinline__ void st(float* p, float x) { *p = x; }
 __device__ __forceinline__ void st(__bf16* p, float x) { *p = static_cast<__bf16>(x); }
 
 template <typename T, int D, bool KEY_IDX>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it,
-                                          float (*__restrict__ s_k)[D], float (*__restrict__ s_v)[D]) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, const UserMeta& um,
+                                          bool indexed, float (*__restrict__ s_k)[D],
+                                          float (*__restrict__ s_v)[D]) {
   constexpr int kKeys = keys_per_tile<D>();
-  const int b = it.x, h = item_head(it), qt = item_tile(it);
-  const UserMeta um = a.meta[b];
+  const int h = item_head(it), qt = item_tile(it);
   const int lane = threadIdx.x;
   const int64_t rs = static_cast<int64_t>(a.H) * D;
   const T* __restrict__ Q = static_cast<const T*>(a.q);
@@ -40,7 +40,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it,
   const int qpos = qt * kLanes + lane;
   const bool qvalid = qpos < um.n_q;
   const int qe = um.q_begin + min(qpos, um.n_q - 1);
-  const int qrow = a.plan->indexed ? a.idx[qe] : qe;
+  const int qrow = indexed ? a.idx[qe] : qe;
   const float sl2 = a.scale_log2;
 
   float q[D], acc[D];
@@ -114,20 +114,19 @@ __global__ __launch_bounds__(kLanes) void k_attn_simple(AttnArgs a) {
   constexpr int kKeys = keys_per_tile<D>();
   __shared__ float s_k[kKeys][D];
   __shared__ float s_v[kKeys][D];
-  if (!plan_matches(a, kLanes)) return;
-  const int item = blockIdx.x;
-  if (item >= a.plan->n_items) return;
-  const int2 it = a.items[item];
+  int2 it;
+  UserMeta um;
+  bool indexed;
+  if (!fetch_item(a, kLanes, blockIdx.x, it, um, indexed)) return;
   if (item_head(it) == kZeroHead) {
-    zero_padding_tile(a, a.meta[it.x], item_tile(it), kLanes, a.H * D * int(sizeof(T)), threadIdx.x,
-                      kLanes);
+    zero_padding_tile(a, um, item_tile(it), kLanes, a.H * D * int(sizeof(T)), threadIdx.x, kLanes);
     return;
   }
   // key rows go through idx[] only for a padded user whose key rows are not one range
-  if (a.plan->indexed && !a.meta[it.x].kv_direct)
-    attn_item<T, D, true>(a, it, s_k, s_v);
+  if (indexed && !um.kv_direct)
+    attn_item<T, D, true>(a, it, um, indexed, s_k, s_v);
   else
-    attn_item<T, D, false>(a, it, s_k, s_v);
+    attn_item<T, D, false>(a, it, um, indexed, s_k, s_v);
 }
 
 template <typename T, int D>

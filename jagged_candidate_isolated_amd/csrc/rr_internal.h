@@ -108,30 +108,44 @@ inline WsLayout ws_layout(int64_t B, int64_t T_idx, int64_t q_rows, int64_t H) {
   return w;
 }
 
-// Arguments of the attention kernels.
+// Arguments of the attention kernels (what every workgroup reads first comes first,
+// so that it arrives in one kernel-argument load).
 struct AttnArgs {
+  const PlanHeader* plan;
+  const int2* items;
+  const UserMeta* meta;
+  int32_t B;
+  int32_t H;
+  int32_t mode;
+  int32_t rows;
   const void* q;       // query rows
   const void* k;       // key rows read by every query of the user
   const void* v;
   const void* k_self;  // own key/value of a candidate, at the query's row
   const void* v_self;
   void* o;
-  const PlanHeader* plan;
-  const UserMeta* meta;
   const int32_t* idx;  // row lists (used when plan->indexed)
-  const int2* items;
-  int32_t B;
-  int32_t H;
-  int32_t mode;
-  int32_t rows;
   float scale_log2;    // softmax scale * log2(e)
 };
 
-// The plan in the workspace matches this launch.
-__device__ __forceinline__ bool plan_matches(const AttnArgs& a, int bm) {
-  const PlanHeader& p = *a.plan;
-  return p.magic == kPlanMagic && p.B == a.B && p.H == a.H && p.bm == bm && p.mode == a.mode &&
-         p.rows == a.rows;
+// The work item of workgroup slot `item` and its user: false when the plan in the
+// workspace does not match this launch or the item is past the list.  The header
+// is read as one 32-byte load and the item next to it, and the user's meta as soon
+// as the item arrives, all before the test, so that a workgroup waits for two
+// memory round trips here rather than one per field.  Both reads stay in bounds
+// whatever the workspace holds: item < gridDim.x <= the items array's length for any
+// launch the host makes for these sizes, and the user index is clamped into [0, B)
+// (B >= 1 whenever a kernel is launched); the values are used only if the test passes.
+__device__ __forceinline__ bool fetch_item(const AttnArgs& a, int bm, int item, int2& it,
+                                           UserMeta& um, bool& indexed) {
+  const PlanHeader p = *a.plan;
+  it = a.items[item];
+  const int b = min(max(it.x, 0), a.B - 1);
+  um = a.meta[b];
+  indexed = p.indexed != 0;
+  return (p.magic == kPlanMagic) & (p.B == a.B) & (p.H == a.H) & (p.bm == bm) &
+         (p.mode == a.mode) & (p.rows == a.rows) & (item < p.n_items) & (b == it.x) &
+         (um.n_q >= 0);   // always true for a listed user; keeps the meta load ahead of the test
 }
 
 // Segment-ID rule of one row (candidate isolation mask page, segment-ID section).
