@@ -47,6 +47,36 @@ def parse_args():
     return p.parse_args()
 
 
+def source_hash() -> str:
+    """Digest of the kernel sources (and the ABI header): traffic counters taken on other
+    sources are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "jagged_candidate_isolated_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "rr.h")]
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed counter summary of
+    this workload (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or
+    None when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"k_attn_mfma_{workload.replace('-', '_')}_traffic.txt")
+    try:
+        with open(path) as fh:
+            for line in fh:
+                f = line.split()
+                if len(f) == 4 and f[0] == "traffic_bytes_per_launch" and f[2] == "sources":
+                    return float(f[1]) if f[3] == source_hash() else None
+    except OSError:
+        pass
+    return None
+
+
 def calibrate_copy(mib: int) -> None:
     """A plain copy kernel of known size, for scaling the HBM traffic counters."""
     import torch
@@ -300,7 +330,7 @@ def main():
         roof = {"bound": "mfma", "achieved": exec_flops / (kernel_ms / 1e3) / 1e12,
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(b.name)
     roof["kernel"] = "k_attn_mfma" if b.dtype == "bf16" and b.d >= 32 else "k_attn_simple"
     roof["kernel_ms"] = kernel_ms
     roof["alg_bytes"] = alg_bytes
