@@ -12,7 +12,9 @@ What it computes (Candidate isolation attention mask page, sections
   3. for every user and head, the explicit [L, L] boolean mask built from the
      segment IDs, then dense softmax attention in float64;
   4. candidate-only layers as the page's fallback: the full layer over the
-     concatenation [frozen history | candidates], keeping the candidate rows.
+     concatenation [frozen history | candidates], keeping the candidate rows;
+  5. right-anchored rotary positions and the rotary encoding of q and k (section
+     "位置编码：候选共用一个位置"; ``rotary.py``).
 
 Readings of the pages where they are silent (each listed in the design notes):
 softmax attention with scale 1/sqrt(d); bidirectional history; rows with no
@@ -29,4 +31,7 @@ from .jagged import offsets_from_lengths, segment_ids, bounds  # noqa: F401
 from .attention import (  # noqa: F401
     isolation_mask_rows, isolation_mask, masked_softmax_attention, full_attention,
     full_attention_rows, cand_only_attention, cand_only_attention_rows, DEFAULT_SCALE,
+)
+from .rotary import (  # noqa: F401
+    right_anchored_positions, rotary_angles, rope, full_attention_rope, cand_only_attention_rope,
 )
