@@ -39,6 +39,9 @@ def parse_args():
     p.add_argument("--config", type=int, default=2,
                    help="2 short-history (default), 3 lognormal, 4 candidate-only, 5 skew, "
                         "6 skew padded (attend_padded_history=True), 7 skew padded (False)")
+    p.add_argument("--rope", action="store_true",
+                   help="rotate q and k at right-anchored positions (rr_rope_qk) inside every step, "
+                        "before the attention")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -128,8 +131,9 @@ def work_counts(cfg, b):
             acc.full_mode_bytes(b.T, b.H, b.d, es), int(b.cand.sum()))
 
 
-def gpu_setup(cfg, b, torch, rr):
-    """Device copies of the inputs (rotated), outputs, the workspace and the two step calls."""
+def gpu_setup(cfg, b, torch, rr, rope=False):
+    """Device copies of the inputs (rotated), outputs, the workspace and the step calls:
+    plan(), run(i) (with the rotary encoding first when ``rope``) and rope_only(i)."""
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if b.dtype == "bf16" else torch.float32
 
@@ -154,29 +158,54 @@ def gpu_setup(cfg, b, torch, rr):
     sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
     outs = [torch.empty_like(out_like) for _ in range(copies)]
 
+    # rotary q / k land in one set of buffers that the attention of the same step reads
+    rot = [torch.empty_like(t) for t in base] if rope else None
     if cfg == 4:
+        hist_len = (hoff[1:] - hoff[:-1]).contiguous()
+        hist_end, cand_first = hoff[1:].contiguous(), coff[:-1].contiguous()
+
         def plan():
             rr.rr_cand_only_plan(hoff, coff, Th, Tc, H, d, dt, workspace=ws)
 
+        def rope_only(i):
+            s = sets[i % copies]
+            rr.rr_rope_qk(None, s[1], hoff, hist_end, k_out=rot[1])
+            rr.rr_rope_qk(s[0], s[3], coff, cand_first, pos_base=hist_len, q_out=rot[0], k_out=rot[3])
+
         def run(i):
             s = sets[i % copies]
-            rr.rr_cand_only_run(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies])
+            if rope:
+                rope_only(i)
+                rr.rr_cand_only_run(rot[0], rot[1], s[2], rot[3], s[4], b.B, ws, out=outs[i % copies])
+            else:
+                rr.rr_cand_only_run(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies])
     else:
         def plan():
             rr.rr_attn_plan(off, cst, b.T, b.H, b.d, dt, valid=valid,
                             attend_padded_history=b.attend_padded_history, workspace=ws)
 
+        def rope_only(i):
+            s = sets[i % copies]
+            rr.rr_rope_qk(s[0], s[1], off, cst, q_out=rot[0], k_out=rot[1])
+
         def run(i):
             s = sets[i % copies]
-            rr.rr_attn_run(s[0], s[1], s[2], b.B, ws, out=outs[i % copies])
-    return plan, run, copies, footprint
+            if rope:
+                rope_only(i)
+                rr.rr_attn_run(rot[0], rot[1], s[2], b.B, ws, out=outs[i % copies])
+            else:
+                rr.rr_attn_run(s[0], s[1], s[2], b.B, ws, out=outs[i % copies])
+    return plan, run, rope_only, copies, footprint
 
 
-def cpu_baseline(cfg, b, budget_s):
+def cpu_baseline(cfg, b, budget_s, rope=False):
     """The oracle, as it stands, on the host cores: whole batches (or the first users of one)
     repeated until about ``budget_s`` of CPU time; effective TFLOP/s of what it finished."""
     import numpy as np
     from oracle import attention as A
+    from oracle import rotary as RO
+    full_fn = RO.full_attention_rope if rope else A.full_attention
+    cand_fn = RO.cand_only_attention_rope if rope else A.cand_only_attention
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -192,19 +221,19 @@ def cpu_baseline(cfg, b, budget_s):
         while time.perf_counter() - t0 < budget_s and users < b.B:
             u = users
             sl = slice(int(coff[u]), int(coff[u + 1]))
-            A.cand_only_attention(b.q_cand[sl], b.k_hist[int(hoff[u]):int(hoff[u + 1])],
+            cand_fn(b.q_cand[sl], b.k_hist[int(hoff[u]):int(hoff[u + 1])],
                                   b.v_hist[int(hoff[u]):int(hoff[u + 1])], b.k_cand[sl], b.v_cand[sl],
                                   [0, int(hl[u])], [0, int(cl[u])])
             done_flops += acc.attention_flops(acc.cand_only_pairs([hl[u]], [cl[u]]), b.H, b.d)
             done_cands += int(cl[u])
             users += 1
-        sample = f"first {users} of {b.B} users, candidate-only oracle"
+        sample = f"first {users} of {b.B} users, candidate-only oracle" + (" with rotary q/k" if rope else "")
     else:
         eff_all, _ = acc.full_mode_counts(b.prefix, b.hist, b.cand, b.pad, b.attend_padded_history)
         small = b.T <= 40000
         while time.perf_counter() - t0 < budget_s:
             if small:
-                A.full_attention(b.q, b.k, b.v, b.offsets, b.cand_start, b.valid, b.attend_padded_history)
+                full_fn(b.q, b.k, b.v, b.offsets, b.cand_start, b.valid, b.attend_padded_history)
                 done_flops += acc.attention_flops(eff_all, b.H, b.d)
                 done_cands += int(b.cand.sum())
                 reps += 1
@@ -215,14 +244,15 @@ def cpu_baseline(cfg, b, budget_s):
                 lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
                 sl = slice(lo, hi)
                 valid = None if b.valid is None else b.valid[sl]
-                A.full_attention(b.q[sl], b.k[sl], b.v[sl], [0, hi - lo], [int(b.cand_start[u]) - lo],
+                full_fn(b.q[sl], b.k[sl], b.v[sl], [0, hi - lo], [int(b.cand_start[u]) - lo],
                                  valid, b.attend_padded_history)
                 e, _ = acc.full_mode_counts(b.prefix[u:u + 1], b.hist[u:u + 1], b.cand[u:u + 1],
                                             b.pad[u:u + 1], b.attend_padded_history)
                 done_flops += acc.attention_flops(e, b.H, b.d)
                 done_cands += int(b.cand[u])
                 users += 1
-        sample = (f"whole batch x{reps}" if small else f"first {users} of {b.B} users") + ", float64 oracle"
+        sample = ((f"whole batch x{reps}" if small else f"first {users} of {b.B} users") + ", float64 oracle"
+                  + (" with rotary q/k" if rope else ""))
     dt = time.perf_counter() - t0
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2), "candidates_per_s": done_cands / dt}
@@ -244,7 +274,7 @@ def main():
     cfg = args.config
     b = make_batch(cfg)
     eff_flops, exec_flops, alg_bytes, n_cands = work_counts(cfg, b)
-    plan, run, copies, footprint = gpu_setup(cfg, b, torch, rr)
+    plan, run, rope_only, copies, footprint = gpu_setup(cfg, b, torch, rr, rope=args.rope)
     torch.cuda.synchronize()
 
     # size the run to about a second of GPU work unless told otherwise
@@ -289,34 +319,42 @@ def main():
     ms_per_step = wall / steps * 1e3
     value = eff_flops / (ms_per_step / 1e3) / 1e12
 
-    # The attention kernel alone: back-to-back launches replayed from a captured graph
-    # (no host gaps), bracketed by HIP events recorded on the launch stream.
+    # One kernel alone: back-to-back launches replayed from a captured graph (no host
+    # gaps), bracketed by HIP events recorded on the launch stream.
     stream = torch.cuda.current_stream()
     plan()
     n_run = copies
-    run_graph = None
-    try:
-        run_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(run_graph):
-            for i in range(n_run):
-                run(i)
-        run_graph.replay()
-    except Exception as e:  # pragma: no cover
-        print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
-        run_graph = None
-    torch.cuda.synchronize()
     reps_k = max(2, math.ceil(max(20, min(steps, 400)) / n_run))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for r in range(reps_k):
-        if run_graph is not None:
-            run_graph.replay()
-        else:
-            for i in range(n_run):
-                run(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    kernel_ms = e0.elapsed_time(e1) / (reps_k * n_run)
+
+    def time_launches(fn):
+        g = None
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n_run):
+                    fn(i)
+            g.replay()
+        except Exception as e:  # pragma: no cover
+            print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
+            g = None
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps_k):
+            if g is not None:
+                g.replay()
+            else:
+                for i in range(n_run):
+                    fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps_k * n_run)
+
+    if args.rope:
+        rope_ms = time_launches(rope_only)
+        kernel_ms = time_launches(run) - rope_ms     # the attention of the rotary step
+    else:
+        kernel_ms = time_launches(run)
 
     flop_per_byte = eff_flops / alg_bytes
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -348,8 +386,17 @@ def main():
         "timing": "hip graph replay" if graph is not None else "eager launches",
         "roofline": roof,
     }
+    if args.rope:
+        es = 2 if b.dtype == "bf16" else 4
+        rows_qk = (b.Tc + b.Th + b.Tc) if cfg == 4 else 2 * b.T      # rows of q and k rotated
+        rope_bytes = 2 * rows_qk * b.H * b.d * es                     # each read once, written once
+        out["rope"] = {"kernel": "k_rope_qk", "kernel_ms": rope_ms, "bound": "hbm",
+                       "achieved": rope_bytes / (rope_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": rope_bytes / (rope_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                       "alg_bytes": rope_bytes}
+        out["config"]["rope"] = "right-anchored rotary q/k, base 10000, inside every step"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, b, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, b, args.cpu_seconds, rope=args.rope)
     print(json.dumps(out), flush=True)
 
 

@@ -170,6 +170,43 @@ int rr_cand_only_run(const void* q_cand, const void* k_hist, const void* v_hist,
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * rr_rope_positions -- right-anchored positions of every row.
+ * Candidate isolation attention mask page, section "位置编码：候选共用一个位置": the
+ * newest history row sits at history_end - 1 whatever the history length, and every
+ * candidate takes the one position history_end.  Rows are numbered within the user's
+ * row [prefix | (pad) | history | candidates] and history_end is the candidate start:
+ *   pos[r] = pos_base[b] + min(r - offsets[b], cand_start[b] - offsets[b])  for r in user b.
+ * pos_base (int32 [B], device, or NULL = all 0) shifts a user's positions: for the
+ * candidate rows of a candidate-only layer pass offsets = cand_offsets,
+ * cand_start = cand_offsets (each user's first candidate row) and pos_base = the frozen
+ * history lengths, so every candidate sits at its user's history end; for the frozen
+ * rows pass cand_start = hist_offsets + 1 (no candidates), so row i sits at i.
+ *
+ * offsets int32 [B+1], cand_start int32 [B], pos_out int32 [T]; all device.
+ */
+int rr_rope_positions(const int32_t* offsets, const int32_t* cand_start, const int32_t* pos_base,
+                      int32_t B, int32_t T, int32_t* pos_out, hipStream_t stream);
+
+/*
+ * rr_rope_qk -- rotary encoding of q and k at right-anchored positions, one pass.
+ * Positions as rr_rope_positions, computed on the fly from offsets / cand_start /
+ * pos_base.  The rotation is the standard pairwise one (a reading: the page names the
+ * rotary encoding without its formula): features (2i, 2i+1) of every head rotate by
+ * pos * theta_base^(-2i/d); the angle is formed and reduced modulo 2 pi in double
+ * precision, its sine and cosine taken in float,
+ * the rotation in float, bf16 results rounded to nearest even.
+ *
+ * q, k         [T][H][d] device inputs; either may be NULL (not rotated)
+ * q_out, k_out [T][H][d] device outputs (required when the input is given); an output
+ *              may be its own input (in place)
+ * d            even, 2 <= d <= 256;  dtype RR_F32 or RR_BF16
+ * theta_base   <= 0 selects 10000
+ */
+int rr_rope_qk(const void* q, const void* k, void* q_out, void* k_out, const int32_t* offsets,
+               const int32_t* cand_start, const int32_t* pos_base, int32_t B, int32_t T, int32_t H,
+               int32_t d, int dtype, float theta_base, hipStream_t stream);
+
+/*
  * rr_validate_jagged -- debug check of the data contract (HSTU scaling notes, section
  * "手算 padding 的浪费与 offset": empty sequences, offset type and user boundaries need
  * checking).  ORs bits into *err_flags (device int32, caller zeroes it first):

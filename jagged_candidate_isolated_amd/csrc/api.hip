@@ -224,6 +224,28 @@ int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_
                           scale, workspace, workspace_bytes, stream);
 }
 
+int rr_rope_positions(const int32_t* offsets, const int32_t* cand_start, const int32_t* pos_base,
+                      int32_t B, int32_t T, int32_t* pos_out, hipStream_t stream) {
+  if (B < 0 || T < 0) return RR_EINVAL;
+  if (B == 0 || T == 0) return RR_OK;
+  if (!offsets || !cand_start || !pos_out) return RR_EINVAL;
+  return status_of(launch_rope_positions(offsets, cand_start, pos_base, B, T, pos_out, stream));
+}
+
+int rr_rope_qk(const void* q, const void* k, void* q_out, void* k_out, const int32_t* offsets,
+               const int32_t* cand_start, const int32_t* pos_base, int32_t B, int32_t T, int32_t H,
+               int32_t d, int dtype, float theta_base, hipStream_t stream) {
+  if (B < 0 || T < 0 || H < 0 || d < 0) return RR_EINVAL;
+  if (dtype != RR_F32 && dtype != RR_BF16) return RR_EDTYPE;
+  if (d % 2 != 0 || d < 2 || d > 256) return RR_EUNSUPPORTED;
+  if (B == 0 || T == 0 || H == 0 || (!q && !k)) return RR_OK;
+  if (!offsets || !cand_start || (q && !q_out) || (k && !k_out)) return RR_EINVAL;
+  if (static_cast<int64_t>(T) * H * d > (int64_t(1) << 40)) return RR_EUNSUPPORTED;
+  const double base = (theta_base > 0.f && isfinite(theta_base)) ? static_cast<double>(theta_base) : 10000.0;
+  return status_of(launch_rope_qk(q, k, q_out, k_out, offsets, cand_start, pos_base, B, T, H, d, dtype,
+                                  log2(base), stream));
+}
+
 int rr_validate_jagged(const int32_t* offsets, const int32_t* cand_start, int32_t B, int32_t T,
                        int32_t* err_flags, hipStream_t stream) {
   if (B < 0 || T < 0) return RR_EINVAL;

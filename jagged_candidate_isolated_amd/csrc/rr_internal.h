@@ -184,6 +184,11 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
                            int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
+hipError_t launch_rope_positions(const int32_t* offsets, const int32_t* cand_start,
+                                 const int32_t* pos_base, int B, int T, int32_t* pos, hipStream_t s);
+hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,
+                          const int32_t* cand_start, const int32_t* pos_base, int B, int T, int H,
+                          int d, int dtype, double log2_base, hipStream_t s);
 
 // Zero the output rows of a padding tile: rows idx[q_begin + n_q + qt*bm ...], every head.
 // `nthreads` threads of the workgroup cooperate; rows are `row_bytes` long (a multiple of 16).

@@ -31,6 +31,9 @@ _SIGS = {
     "rr_cand_only_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                              ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "rr_validate_jagged": (ctypes.c_int, [_P, _P, _I, _I, _P, _P]),
+    "rr_rope_positions": (ctypes.c_int, [_P, _P, _P, _I, _I, _P, _P]),
+    "rr_rope_qk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int,
+                                  ctypes.c_float, _P]),
     "rr_attn_plan": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int, _P,
                                     ctypes.c_size_t, _P]),
     "rr_attn_run": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float, _P,
@@ -298,3 +301,58 @@ def rr_validate_jagged(offsets, cand_start, T: int, stream=None) -> int:
     _check("rr_validate_jagged", _lib.rr_validate_jagged(_ptr(offsets), _ptr(cand_start),
                                                          offsets.numel() - 1, T, _ptr(err), s))
     return int(err.item())
+
+
+def rr_rope_positions(offsets, cand_start, T: int, pos_base=None, out=None, stream=None) -> torch.Tensor:
+    """Right-anchored position of every row (int32 [T])."""
+    dev = offsets.device
+    _need(offsets, "offsets", torch.int32)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if pos_base is not None:
+        _need(pos_base, "pos_base", torch.int32, dev)
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty(T, dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, dev)
+    _check("rr_rope_positions", _lib.rr_rope_positions(_ptr(offsets), _ptr(cand_start), _ptr(pos_base),
+                                                       B, T, _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def rr_rope_qk(q, k, offsets, cand_start, pos_base=None, theta_base=None, q_out=None, k_out=None,
+               in_place=False, stream=None):
+    """Rotary encoding of q and k ([T, H, d], either may be None) at right-anchored positions.
+
+    Returns (q_out, k_out); with ``in_place`` the inputs are overwritten and returned."""
+    x = q if q is not None else k
+    if x is None:
+        return None, None
+    dev = x.device
+    _need(x, "q" if q is not None else "k")
+    dt = _rr_dtype(x)
+    if x.dim() != 3:
+        raise ValueError("q and k must be [T, H, d]")
+    T, H, d = x.shape
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if pos_base is not None:
+        _need(pos_base, "pos_base", torch.int32, dev)
+    outs = []
+    for name, t, o in (("q", q, q_out), ("k", k, k_out)):
+        if t is None:
+            outs.append(None)
+            continue
+        _need(t, name, x.dtype, dev)
+        if t.shape != x.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(x.shape)}")
+        if o is None:
+            o = t if in_place else torch.empty_like(t)
+        _need(o, f"{name}_out", x.dtype, dev)
+        if o.shape != x.shape:
+            raise ValueError(f"{name}_out shape {tuple(o.shape)} != {tuple(x.shape)}")
+        outs.append(o)
+    B = offsets.numel() - 1
+    _check("rr_rope_qk", _lib.rr_rope_qk(_ptr(q), _ptr(k), _ptr(outs[0]), _ptr(outs[1]), _ptr(offsets),
+                                         _ptr(cand_start), _ptr(pos_base), B, T, H, d, dt,
+                                         float(theta_base or 0.0), _stream(stream, dev)))
+    return outs[0], outs[1]

@@ -108,6 +108,31 @@ def test_segment_and_bounds_argument_errors():
     assert lib.rr_validate_jagged(None, None, 1, 1, FAKE, None) == rr.RR_EINVAL
 
 
+def test_rope_argument_errors():
+    rr, lib = _lib()
+    # (q, k, q_out, k_out, offsets, cand_start, pos_base, B, T, H, d, dtype, base, stream)
+    ok = dict(q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, off=FAKE, cs=FAKE, B=2, T=8, H=2, d=64, dt=rr.RR_BF16)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.rr_rope_qk(a["q"], a["k"], a["qo"], a["ko"], a["off"], a["cs"], None, a["B"], a["T"],
+                              a["H"], a["d"], a["dt"], 0.0, None)
+    assert call(d=63) == rr.RR_EUNSUPPORTED
+    assert call(d=0) == rr.RR_EUNSUPPORTED
+    assert call(d=258) == rr.RR_EUNSUPPORTED
+    assert call(dt=7) == rr.RR_EDTYPE
+    assert call(B=-1) == rr.RR_EINVAL
+    assert call(qo=None) == rr.RR_EINVAL
+    assert call(ko=None) == rr.RR_EINVAL
+    assert call(off=None) == rr.RR_EINVAL
+    assert call(q=None, k=None) == rr.RR_OK          # nothing to rotate: no launch
+    assert call(B=0) == rr.RR_OK and call(T=0) == rr.RR_OK
+    assert lib.rr_rope_positions(None, FAKE, None, 2, 8, FAKE, None) == rr.RR_EINVAL
+    assert lib.rr_rope_positions(FAKE, FAKE, None, 2, 8, None, None) == rr.RR_EINVAL
+    assert lib.rr_rope_positions(FAKE, FAKE, None, -1, 8, FAKE, None) == rr.RR_EINVAL
+    assert lib.rr_rope_positions(None, None, None, 0, 0, None, None) == rr.RR_OK
+
+
 def test_workspace_size_grows_with_work():
     _, lib = _lib()
     a = lib.rr_attn_workspace_bytes(64, 16000, 4, 64)
