@@ -14,7 +14,9 @@ What it computes (Candidate isolation attention mask page, sections
   4. candidate-only layers as the page's fallback: the full layer over the
      concatenation [frozen history | candidates], keeping the candidate rows;
   5. right-anchored rotary positions and the rotary encoding of q and k (section
-     "位置编码：候选共用一个位置"; ``rotary.py``).
+     "位置编码：候选共用一个位置"; ``rotary.py``);
+  6. the gradients of the attention w.r.t. q, k, v and each row's log-sum-exp
+     (``backward.py``), from the forward's definition and the softmax derivative.
 
 Readings of the pages where they are silent (each listed in the design notes):
 softmax attention with scale 1/sqrt(d); bidirectional history; rows with no
@@ -35,3 +37,4 @@ from .attention import (  # noqa: F401
 from .rotary import (  # noqa: F401
     right_anchored_positions, rotary_angles, rope, full_attention_rope, cand_only_attention_rope,
 )
+from .backward import full_attention_backward, attention_lse  # noqa: F401

@@ -1,0 +1,83 @@
+"""Oracle: gradients of the candidate-isolated attention in float64 (test infrastructure only).
+
+The pages train with this mask too (Candidate isolation attention mask page, section
+"训练时的序列打包": sequence packing keeps the same attention contract), but they
+print no backward formulas.  The gradients here are those of the forward oracle's
+definition -- per user and head, P = softmax(scale * q k^T masked by the explicit
+[L, L] isolation mask), O = P v -- taken with the textbook softmax derivative:
+
+    dV = P^T dO
+    dP = dO v^T
+    dS = P * (dP - rowsum(dP * P))          (elementwise; masked entries have P = 0)
+    dq = scale * dS k,   dk = scale * dS^T q
+
+Rows that admit no key (segment 0) have P = 0: they get no gradient and give none.
+``attention_lse`` gives each row's log-sum-exp of its admitted scaled scores (natural
+log), the statistic a backward pass reuses from the forward; -inf for such rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _scale, isolation_mask
+from .jagged import segment_ids
+
+
+def _user_head_backward(q, k, v, do, mask, sc):
+    """One user and head: returns dq, dk, dv (float64) for the [L, L] ``mask``."""
+    s = sc * (q @ k.T)
+    s = np.where(mask, s, -np.inf)
+    has = mask.any(axis=1)
+    p = np.zeros_like(s)
+    if has.any():
+        m = s[has].max(axis=1, keepdims=True)
+        e = np.where(mask[has], np.exp(s[has] - m), 0.0)
+        p[has] = e / e.sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    return sc * (ds @ k), sc * (ds.T @ q), dv
+
+
+def full_attention_backward(q, k, v, do, offsets, cand_start, valid=None, attend_padded_history=False,
+                            scale=None):
+    """Gradients (dq, dk, dv) of full-sequence attention w.r.t. q, k, v for output gradient
+    ``do``; all [T, H, d] float64."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64); do = np.asarray(do, np.float64)
+    T, H, d = q.shape
+    sc = _scale(scale, d)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    seg = segment_ids(offsets, cand_start, valid, attend_padded_history)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi == lo:
+            continue
+        mask = isolation_mask(seg[lo:hi])
+        for h in range(H):
+            dq[lo:hi, h], dk[lo:hi, h], dv[lo:hi, h] = _user_head_backward(
+                q[lo:hi, h], k[lo:hi, h], v[lo:hi, h], do[lo:hi, h], mask, sc)
+    return dq, dk, dv
+
+
+def attention_lse(q, k, offsets, cand_start, valid=None, attend_padded_history=False, scale=None):
+    """Per (row, head) natural-log sum of exp(scale * q.k) over the row's admitted keys;
+    float64 [T, H], -inf for rows that admit none."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    T, H, d = q.shape
+    sc = _scale(scale, d)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    seg = segment_ids(offsets, cand_start, valid, attend_padded_history)
+    out = np.full((T, H), -np.inf)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi == lo:
+            continue
+        mask = isolation_mask(seg[lo:hi])
+        has = mask.any(axis=1)
+        for h in range(H):
+            s = np.where(mask, sc * (q[lo:hi, h] @ k[lo:hi, h].T), -np.inf)[has]
+            m = s.max(axis=1)
+            out[lo:hi, h][has] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out

@@ -1,0 +1,159 @@
+"""Pins for the backward oracle (oracle/backward.py).
+
+Each ``pin_*`` raises AssertionError when the oracle's gradients disagree with
+ * central finite differences of the (separately pinned) forward oracle,
+ * torch autograd through torch's CPU scaled_dot_product_attention in float64, with the
+   admitted key sets written here from the plain-language rule (a library routine),
+ * exactly rounded log-sum-exp sums (math.fsum) for ``attention_lse``,
+ * closed forms (a one-row user; a candidate's own key and value), or
+ * the page's isolation invariants carried over to gradients.
+They call the oracle through its modules at call time, so tests can plant mistakes.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import attention as A
+from oracle import backward as G
+from _pins import rng_for, tiny_batches
+from workloads import make_full_batch
+
+
+def _grads(fb, do, scale=None):
+    return G.full_attention_backward(fb.q, fb.k, fb.v, do, fb.offsets, fb.cand_start, fb.valid,
+                                     fb.attend_padded_history, scale)
+
+
+def pin_finite_differences():
+    """d(sum(O * dO))/dx by central differences of the forward oracle, every entry of
+    every tiny batch (holes, empty users, padding with both flags)."""
+    eps = 1e-6
+    for fb in tiny_batches():
+        q, k, v = (np.asarray(x, np.float64) for x in (fb.q, fb.k, fb.v))
+        rng = rng_for(91)
+        do = rng.standard_normal(q.shape)
+
+        def loss(qq, kk, vv):
+            o = A.full_attention(qq, kk, vv, fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history)
+            return float(np.sum(o * do))
+        got = G.full_attention_backward(q, k, v, do, fb.offsets, fb.cand_start, fb.valid,
+                                        fb.attend_padded_history)
+        for which, x in enumerate((q, k, v)):
+            num = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                i = it.multi_index
+                xp, xm = x.copy(), x.copy()
+                xp[i] += eps; xm[i] -= eps
+                args_p = [q, k, v]; args_p[which] = xp
+                args_m = [q, k, v]; args_m[which] = xm
+                num[i] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            err = np.max(np.abs(num - got[which]))
+            assert err <= 1e-6 * (1 + np.max(np.abs(num))), (fb.name, "qkv"[which], err)
+
+
+def pin_torch_autograd():
+    """Gradients through torch's fp64 SDPA with a boolean mask written from the rule:
+    history rows see the user's history, candidates see the history and themselves."""
+    import torch
+    F = torch.nn.functional
+    rng = rng_for(92)
+    fb = make_full_batch(rng, "bwd-sdpa", prefix=[1, 3, 0], hist=[4, 2, 3], cand=[3, 2, 0], H=2, d=8,
+                         dtype="f32", scaled=False)
+    do = rng.standard_normal(fb.q.shape)
+    dq, dk, dv = _grads(fb, do)
+    for b in range(fb.B):
+        lo, cs, hi = int(fb.offsets[b]), int(fb.cand_start[b]), int(fb.offsets[b + 1])
+        L = hi - lo
+        allowed = np.zeros((L, L), dtype=bool)
+        for i in range(L):
+            for j in range(cs - lo):
+                allowed[i, j] = True          # everyone sees the history
+            if i >= cs - lo:
+                allowed[i, i] = True          # a candidate also sees itself
+        t = [torch.from_numpy(np.ascontiguousarray(x[lo:hi].transpose(1, 0, 2))).double().requires_grad_()
+             for x in (fb.q, fb.k, fb.v)]
+        o = F.scaled_dot_product_attention(*t, attn_mask=torch.from_numpy(allowed))
+        o.backward(torch.from_numpy(np.ascontiguousarray(do[lo:hi].transpose(1, 0, 2))))
+        for g_t, mine in zip(t, (dq, dk, dv)):
+            ref = g_t.grad.numpy().transpose(1, 0, 2)
+            assert np.max(np.abs(ref - mine[lo:hi])) <= 1e-11, b
+
+
+def pin_lse():
+    for fb in tiny_batches():
+        lse = G.attention_lse(fb.q, fb.k, fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history)
+        sc = 1.0 / math.sqrt(fb.d)
+        from oracle.jagged import segment_ids
+        seg = segment_ids(fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history)
+        for b in range(fb.B):
+            lo, hi = int(fb.offsets[b]), int(fb.offsets[b + 1])
+            for i in range(lo, hi):
+                if seg[i] == 0:
+                    keys = []
+                else:
+                    keys = [j for j in range(lo, hi) if seg[j] == 1] + ([i] if seg[i] == -1 else [])
+                for h in range(fb.H):
+                    if not keys:
+                        assert lse[i, h] == -np.inf
+                        continue
+                    s = [sc * math.fsum(float(fb.q[i, h, t]) * float(fb.k[j, h, t]) for t in range(fb.d))
+                         for j in keys]
+                    m = max(s)
+                    want = m + math.log(math.fsum(math.exp(x - m) for x in s))
+                    assert abs(lse[i, h] - want) <= 1e-12, (fb.name, i, h)
+
+
+def pin_closed_forms():
+    rng = rng_for(93)
+    # a one-row user (its own single key): P = 1, so dv = do and dq = dk = 0
+    fb = make_full_batch(rng, "one-row", prefix=[1, 0], hist=[0, 0], cand=[0, 1], H=2, d=4,
+                         dtype="f32", scaled=False)
+    do = rng.standard_normal(fb.q.shape)
+    dq, dk, dv = _grads(fb, do)
+    assert np.max(np.abs(dv - do)) <= 1e-15 and np.max(np.abs(dq)) == 0 and np.max(np.abs(dk)) == 0
+    # a candidate's own key and value are read only by that candidate:
+    # dv_c = p_cc do_c and dk_c = scale * p_cc (do_c . (v_c - o_c)) q_c
+    fb = make_full_batch(rng, "cand-own", prefix=[2], hist=[3], cand=[4], H=1, d=6, dtype="f32",
+                         scaled=False)
+    do = rng.standard_normal(fb.q.shape)
+    dq, dk, dv = _grads(fb, do)
+    o = A.full_attention(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start)
+    lse = G.attention_lse(fb.q, fb.k, fb.offsets, fb.cand_start)
+    sc = 1.0 / math.sqrt(fb.d)
+    for c in range(int(fb.cand_start[0]), fb.T):
+        qc, kc, vc = (np.asarray(x[c, 0], np.float64) for x in (fb.q, fb.k, fb.v))
+        p = math.exp(sc * float(np.dot(qc, kc)) - lse[c, 0])
+        assert np.max(np.abs(dv[c, 0] - p * do[c, 0])) <= 1e-12
+        want = sc * p * float(np.dot(do[c, 0], vc - o[c, 0])) * qc
+        assert np.max(np.abs(dk[c, 0] - want)) <= 1e-12
+
+
+def pin_isolation_of_gradients():
+    """Gradients of one user never depend on another user's values; padding rows (flag
+    False) get none; a candidate's output gradient never reaches other candidates' k, v."""
+    rng = rng_for(94)
+    fb = make_full_batch(rng, "iso", prefix=[1, 2], hist=[3, 2], cand=[3, 2], pad=[2, 0], H=2, d=4,
+                         dtype="f32", scaled=False)
+    do = rng.standard_normal(fb.q.shape)
+    g0 = _grads(fb, do)
+    q2 = fb.q.copy(); q2[int(fb.offsets[1]):] *= 3.0
+    g1 = G.full_attention_backward(q2, fb.k, fb.v, do, fb.offsets, fb.cand_start, fb.valid)
+    lo1 = int(fb.offsets[1])
+    for a, b in zip(g0, g1):
+        assert np.array_equal(a[:lo1], b[:lo1])
+    pad = np.nonzero(fb.valid == 0)[0]
+    for g in g0:
+        assert np.all(g[pad] == 0)
+    # output gradient on one candidate only: other candidates' k and v get nothing
+    c0 = int(fb.cand_start[0])
+    do1 = np.zeros_like(do); do1[c0] = do[c0]
+    dq, dk, dv = _grads(fb, do1)
+    others = [c for c in range(c0 + 1, lo1)]
+    assert np.all(dk[others] == 0) and np.all(dv[others] == 0)
+
+
+BWD_PINS = [pin_finite_differences, pin_torch_autograd, pin_lse, pin_closed_forms,
+            pin_isolation_of_gradients]

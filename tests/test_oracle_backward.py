@@ -1,0 +1,49 @@
+"""The backward oracle against its pins, and planted mistakes that some pin catches (CPU)."""
+import numpy as np
+import pytest
+
+import _bwd_pins
+from oracle import backward as G
+
+
+@pytest.mark.parametrize("pin", _bwd_pins.BWD_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def _user_factory(kind):
+    def f(q, k, v, do, mask, sc):
+        s = np.where(mask, sc * (q @ k.T), -np.inf)
+        has = mask.any(axis=1)
+        p = np.zeros_like(s)
+        if has.any():
+            m = s[has].max(axis=1, keepdims=True)
+            e = np.where(mask[has], np.exp(s[has] - m), 0.0)
+            p[has] = e / e.sum(axis=1, keepdims=True)
+        dv = (p @ do) if kind == "dv_not_transposed" else p.T @ do
+        dp = do @ v.T
+        if kind == "no_rowsum":
+            ds = p * dp
+        else:
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+        dq = (ds @ k) if kind == "dq_unscaled" else sc * (ds @ k)
+        dk = sc * (ds @ q) if kind == "dk_not_transposed" else sc * (ds.T @ q)
+        if kind == "dv_from_values":
+            dv = p.T @ v
+        return dq, dk, dv
+    return f
+
+
+MUTATIONS = ["no_rowsum", "dv_not_transposed", "dq_unscaled", "dk_not_transposed", "dv_from_values"]
+
+
+@pytest.mark.parametrize("name", MUTATIONS)
+def test_some_pin_catches(name, monkeypatch):
+    monkeypatch.setattr(G, "_user_head_backward", _user_factory(name))
+    caught = []
+    for pin in _bwd_pins.BWD_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutation {name}"
