@@ -137,6 +137,53 @@ int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B,
                 int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * rr_attn_run_lse -- rr_attn_run that also writes each row's log-sum-exp.
+ * lse  float [T][H] device, written: the natural log of the sum of exp(scale * q.k)
+ *      over the keys row r reads in head h (-inf for segment-0 rows).  The backward
+ *      pass recomputes the softmax from it.  NULL = not written (then as rr_attn_run).
+ */
+int rr_attn_run_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                    int32_t T, int32_t H, int32_t d, int dtype, float scale, const void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward pass of full-sequence candidate-isolated attention.
+ * Candidate isolation attention mask page, section "训练时的序列打包" (training keeps the
+ * same attention contract; the page prints no gradient formulas).  The gradients are
+ * those of the forward's definition, with the softmax recomputed from the forward's
+ * lse:  P = exp(scale q.k - lse),  dv = P^T dO,  dP = dO v^T,
+ *       dS = P (dP - rowsum(dO * o)),  dq = scale dS k,  dk = scale dS^T q.
+ * A history key's dk, dv sum over every valid query of its user; a candidate's own
+ * key and value get gradients from that candidate alone; segment-0 rows get 0.  Every
+ * output element is written by one workgroup without atomics: repeated calls give the
+ * same bits.  Supported: dtype RR_BF16 and d in {64, 128} (other valid sizes return
+ * RR_EUNSUPPORTED); accumulation is fp32.
+ *
+ * Two steps, as the forward's: rr_attn_plan into a workspace of
+ * rr_attn_bwd_workspace_bytes (which also holds rowsum(dO * o) between the two kernels
+ * of the backward), rr_attn_run_lse for o and lse, then rr_attn_bwd_run over the same
+ * plan.  rr_attn_bwd plans and runs the backward in one call.
+ *
+ * q, k, v     [T][H][d] bf16 device, the forward's inputs
+ * o           [T][H][d] bf16 device, the forward's output for these inputs and scale
+ * dout        [T][H][d] bf16 device, gradient of the loss w.r.t. o
+ * lse         float [T][H] device, from rr_attn_run_lse on these inputs and scale
+ * dq, dk, dv  [T][H][d] bf16 device, written (every row, 0 for segment-0 rows); they
+ *             must not alias any input
+ * offsets, cand_start, valid, attend_padded_history, scale: as rr_attn_fwd
+ */
+size_t rr_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d);
+int rr_attn_bwd_run(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t T, int32_t H,
+                    int32_t d, int dtype, float scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+int rr_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, const int32_t* offsets,
+                const int32_t* cand_start, const uint8_t* valid, int attend_padded_history, int32_t B,
+                int32_t T, int32_t H, int32_t d, int dtype, float scale, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace rr_cand_only_attn_fwd needs for these sizes (0 on invalid sizes). */
 size_t rr_cand_only_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d);
 

@@ -103,17 +103,17 @@ size_t rr_attn_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d) {
   return ws_layout(B, T, T, H).total;
 }
 
-int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
-                 int attend_padded_history, int32_t B, int32_t T, int32_t H, int32_t d, int dtype,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const int st = check_sizes(B, T, T, H, d, dtype);
-  if (st != RR_OK) return st;
-  if (B == 0 || T == 0 || H == 0) return RR_OK;
-  if (!offsets || !cand_start) return RR_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// The plan of a full-sequence call for tiles of `bm` query rows, into a workspace the
+// caller has checked.
+int plan_full(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+              int attend_padded_history, int32_t B, int32_t T, int32_t H, int bm, void* workspace,
+              hipStream_t stream) {
   const WsLayout w = ws_layout(B, T, T, H);
-  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
   const Ws p = carve_all(workspace, w);
-  const int bm = tile_rows(dtype, d, B, T);
   const int64_t cap = attn_grid(B, T, H, bm);   // <= w.item_bound
   hipError_t e = hipSuccess;
   if (valid) {
@@ -131,22 +131,97 @@ int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_
   return status_of(e);
 }
 
-int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T, int32_t H,
-                int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
-  const int st = check_sizes(B, T, T, H, d, dtype);
-  if (st != RR_OK) return st;
-  if (B == 0 || T == 0 || H == 0) return RR_OK;
-  if (!q || !k || !v || !o) return RR_EINVAL;
-  const WsLayout w = ws_layout(B, T, T, H);
-  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
-  const Ws p = carve_all(const_cast<void*>(workspace), w);
+// Forward arguments of a full-sequence run over a planned workspace.
+AttnArgs full_args(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T,
+                   int32_t H, int32_t d, float scale, const void* workspace) {
+  const Ws p = carve_all(const_cast<void*>(workspace), ws_layout(B, T, T, H));
   AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.k_self = k; a.v_self = v; a.o = o;
   a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
   a.B = B; a.H = H; a.mode = 0; a.rows = T;
   a.scale_log2 = softmax_scale_log2(scale, d);
+  return a;
+}
+
+bool bwd_supported(int dtype, int d) { return dtype == RR_BF16 && (d == 64 || d == 128); }
+
+size_t bwd_delta_offset(int32_t B, int32_t T, int32_t H) { return align256(ws_layout(B, T, T, H).total); }
+
+}  // namespace
+
+extern "C" {
+
+int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
+                 int attend_padded_history, int32_t B, int32_t T, int32_t H, int32_t d, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!offsets || !cand_start) return RR_EINVAL;
+  if (!workspace || workspace_bytes < ws_layout(B, T, T, H).total) return RR_EWORKSPACE;
+  return plan_full(offsets, cand_start, valid, attend_padded_history, B, T, H, tile_rows(dtype, d, B, T),
+                   workspace, stream);
+}
+
+int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T, int32_t H,
+                int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  return rr_attn_run_lse(q, k, v, o, nullptr, B, T, H, d, dtype, scale, workspace, workspace_bytes,
+                         stream);
+}
+
+int rr_attn_run_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                    int32_t T, int32_t H, int32_t d, int dtype, float scale, const void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!q || !k || !v || !o) return RR_EINVAL;
+  if (!workspace || workspace_bytes < ws_layout(B, T, T, H).total) return RR_EWORKSPACE;
+  AttnArgs a = full_args(q, k, v, o, B, T, H, d, scale, workspace);
+  a.lse = lse;
   return run_attention(a, dtype, d, tile_rows(dtype, d, B, T), T, stream);
+}
+
+size_t rr_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d) {
+  if (check_sizes(B, T, T, H, d, RR_BF16) != RR_OK || !bwd_supported(RR_BF16, d)) return 0;
+  return bwd_delta_offset(B, T, H) + align256(sizeof(float) * size_t(T) * size_t(H));
+}
+
+int rr_attn_bwd_run(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t T, int32_t H,
+                    int32_t d, int dtype, float scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (!bwd_supported(dtype, d)) return RR_EUNSUPPORTED;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return RR_EINVAL;
+  if (!workspace || workspace_bytes < rr_attn_bwd_workspace_bytes(B, T, H, d)) return RR_EWORKSPACE;
+  const AttnArgs a = full_args(q, k, v, const_cast<void*>(o), B, T, H, d, scale, workspace);
+  float* delta = carve<float>(workspace, bwd_delta_offset(B, T, H));
+  const float sc = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf(static_cast<float>(d));
+  const int bm = tile_rows(dtype, d, B, T);   // the plan rr_attn_plan made for these sizes
+  return status_of(launch_attn_bwd(a, dout, lse, dq, dk, dv, delta, sc, d, bm, attn_grid(B, T, H, bm),
+                                   stream));
+}
+
+int rr_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, const int32_t* offsets,
+                const int32_t* cand_start, const uint8_t* valid, int attend_padded_history, int32_t B,
+                int32_t T, int32_t H, int32_t d, int dtype, float scale, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (!bwd_supported(dtype, d)) return RR_EUNSUPPORTED;
+  if (B == 0 || T == 0 || H == 0) return RR_OK;
+  if (!offsets || !cand_start) return RR_EINVAL;
+  if (!workspace || workspace_bytes < rr_attn_bwd_workspace_bytes(B, T, H, d)) return RR_EWORKSPACE;
+  const int r = rr_attn_plan(offsets, cand_start, valid, attend_padded_history, B, T, H, d, dtype,
+                             workspace, workspace_bytes, stream);
+  if (r != RR_OK) return r;
+  return rr_attn_bwd_run(q, k, v, o, dout, lse, dq, dk, dv, B, T, H, d, dtype, scale, workspace,
+                         workspace_bytes, stream);
 }
 
 int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,

@@ -248,9 +248,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     }
   }
   sd = halves_sum(sd);
+  float mref = m_i;   // the reference the row's sum l_tot is taken against (log2 units)
   if (qpos >= um.cand_rel) {
     const float ts = sd * sl2;
     const float mn = fmaxf(m_i, ts);
+    mref = mn;
     const float al = __builtin_amdgcn_exp2f(m_i - mn);
     const float be = __builtin_amdgcn_exp2f(ts - mn);
     l_tot = l_tot * al + be;
@@ -268,6 +270,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   }
 
   if (qvalid) {
+    if (a.lse && half == 0)
+      a.lse[static_cast<int64_t>(qrow) * a.H + h] =
+          l_tot > 0.f ? (mref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

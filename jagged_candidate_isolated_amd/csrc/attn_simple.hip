@@ -101,8 +101,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     l = l * alpha + beta;
 #pragma unroll
     for (int e = 0; e < D; ++e) acc[e] = acc[e] * alpha + beta * ld(VS + qrow * rs + h * D + e);
+    m = m_new;
   }
   if (qvalid) {
+    if (a.lse)
+      a.lse[static_cast<int64_t>(qrow) * a.H + h] =
+          l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int e = 0; e < D; ++e) st(O + qrow * rs + h * D + e, acc[e] * inv);

@@ -119,6 +119,17 @@ __device__ __forceinline__ void lds_dma_global16(const void* gptr, uint32_t lds_
       : "memory", "m0");
 }
 
+// 4-byte variant: lane l writes its 4 bytes to lds_addr + 4 l.
+__device__ __forceinline__ void lds_dma_global4(const void* gptr, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off"
+      :
+      : "s"(lds_addr), "v"(gptr)
+      : "memory", "m0");
+}
+
 // LDS address (byte offset in the workgroup's LDS) of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS const void*)p));
@@ -226,6 +237,26 @@ struct KvLoader {
         const int64_t g = static_cast<int64_t>(KEY_IDX ? idx[e] : e) * rs2 +
                           (ld_off[i] - static_cast<uint32_t>(row * rs2));
         lds_dma_global16(reinterpret_cast<const char*>(kp) + g, lk + i * 1024);
+        lds_dma_global16(reinterpret_cast<const char*>(vp) + g, lv + i * 1024);
+      }
+    }
+  }
+
+  // the value rows of tile t only, into dv
+  __device__ __forceinline__ void issue_v(int t, u16* dv) const {
+    const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_address(dv + lds_base));
+    if (ranged && (t + 1) * BN <= n_kv) {
+      const int64_t tile_off = static_cast<int64_t>(t) * BN * rs2;
+      const v4i32 v_rsrc = byte_range(v_user + tile_off, static_cast<uint32_t>(user_bytes - tile_off));
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) lds_dma_buffer16(v_rsrc, ld_off[i], lv + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int row = ld_row[i];
+        const int e = kv_begin + min(t * BN + row, n_kv - 1);
+        const int64_t g = static_cast<int64_t>(KEY_IDX ? idx[e] : e) * rs2 +
+                          (ld_off[i] - static_cast<uint32_t>(row * rs2));
         lds_dma_global16(reinterpret_cast<const char*>(vp) + g, lv + i * 1024);
       }
     }

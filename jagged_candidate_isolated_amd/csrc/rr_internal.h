@@ -126,6 +126,7 @@ struct AttnArgs {
   void* o;
   const int32_t* idx;  // row lists (used when plan->indexed)
   float scale_log2;    // softmax scale * log2(e)
+  float* lse;          // [rows][H] natural-log sum of exp(scale q.k) over each row's keys, or NULL
 };
 
 // The work item of workgroup slot `item` and its user: false when the plan in the
@@ -184,13 +185,17 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
                            int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dk,
+                           void* dv, float* delta, float scale, int d, int bm, int64_t grid,
+                           hipStream_t s);
 hipError_t launch_rope_positions(const int32_t* offsets, const int32_t* cand_start,
                                  const int32_t* pos_base, int B, int T, int32_t* pos, hipStream_t s);
 hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,
                           const int32_t* cand_start, const int32_t* pos_base, int B, int T, int H,
                           int d, int dtype, double log2_base, hipStream_t s);
 
-// Zero the output rows of a padding tile: rows idx[q_begin + n_q + qt*bm ...], every head.
+// Zero the output rows of a padding tile: rows idx[q_begin + n_q + qt*bm ...], every head
+// (and set their log-sum-exp to -inf when the forward writes it).
 // `nthreads` threads of the workgroup cooperate; rows are `row_bytes` long (a multiple of 16).
 __device__ __forceinline__ void zero_padding_tile(const AttnArgs& a, const UserMeta& um, int qt,
                                                   int bm, int row_bytes, int tid, int nthreads) {
@@ -202,6 +207,11 @@ __device__ __forceinline__ void zero_padding_tile(const AttnArgs& a, const UserM
     const int r = a.idx[um.q_begin + um.n_q + first + e / chunks];
     o[static_cast<int64_t>(r) * chunks + (e % chunks)] = make_uint4(0, 0, 0, 0);
   }
+  if (a.lse)   // a padding row admits no key: its log-sum-exp is -inf in every head
+    for (int e = tid; e < nrows * a.H; e += nthreads) {
+      const int r = a.idx[um.q_begin + um.n_q + first + e / a.H];
+      a.lse[static_cast<int64_t>(r) * a.H + (e % a.H)] = -INFINITY;
+    }
 }
 
 }  // namespace rr

@@ -38,6 +38,13 @@ _SIGS = {
                                     ctypes.c_size_t, _P]),
     "rr_attn_run": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float, _P,
                                    ctypes.c_size_t, _P]),
+    "rr_attn_run_lse": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float,
+                                       _P, ctypes.c_size_t, _P]),
+    "rr_attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "rr_attn_bwd_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int,
+                                       ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I, _I,
+                                   _I, _I, ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "rr_cand_only_plan": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P,
                                          ctypes.c_size_t, _P]),
     "rr_cand_only_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
@@ -223,8 +230,10 @@ def rr_cand_only_attn_fwd(q_cand, k_hist, v_hist, k_cand, v_cand, hist_offsets, 
 
 
 def rr_attn_plan(offsets, cand_start, T: int, H: int, d: int, dtype, valid=None,
-                 attend_padded_history=False, workspace=None, stream=None) -> torch.Tensor:
-    """Plan a full-sequence call (lengths only); returns the workspace holding the plan."""
+                 attend_padded_history=False, workspace=None, stream=None,
+                 backward=False) -> torch.Tensor:
+    """Plan a full-sequence call (lengths only); returns the workspace holding the plan.
+    ``backward`` sizes a new workspace for rr_attn_bwd_run as well."""
     dev = offsets.device
     _need(offsets, "offsets", torch.int32)
     _need(cand_start, "cand_start", torch.int32, dev)
@@ -232,7 +241,8 @@ def rr_attn_plan(offsets, cand_start, T: int, H: int, d: int, dtype, valid=None,
         _need(valid, "valid", torch.uint8, dev)
     B = offsets.numel() - 1
     dt = _rr_dtype(torch.empty(0, dtype=dtype))
-    ws = _workspace(rr_attn_workspace_bytes(B, T, H, d), workspace, dev)
+    need = rr_attn_bwd_workspace_bytes(B, T, H, d) if backward else rr_attn_workspace_bytes(B, T, H, d)
+    ws = _workspace(need, workspace, dev)
     _check("rr_attn_plan", _lib.rr_attn_plan(_ptr(offsets), _ptr(cand_start), _ptr(valid),
                                              int(bool(attend_padded_history)), B, T, H, d, dt,
                                              _ptr(ws), ws.numel(), _stream(stream, dev)))
@@ -255,6 +265,85 @@ def rr_attn_run(q, k, v, B: int, workspace, scale=None, out=None, stream=None) -
                                            float(scale or 0.0), _ptr(workspace), workspace.numel(),
                                            _stream(stream, dev)))
     return out
+
+
+def rr_attn_run_lse(q, k, v, B: int, workspace, scale=None, out=None, lse=None, stream=None):
+    """rr_attn_run that also returns each row's log-sum-exp: (out, lse float32 [T, H])."""
+    dev = q.device
+    _need(q, "q")
+    dt = _rr_dtype(q)
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    T, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _check("rr_attn_run_lse", _lib.rr_attn_run_lse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, d, dt, float(scale or 0.0),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return out, lse
+
+
+def rr_attn_bwd_workspace_bytes(B: int, T: int, H: int, d: int) -> int:
+    return int(_lib.rr_attn_bwd_workspace_bytes(B, T, H, d))
+
+
+def _bwd_tensors(q, k, v, o, dout, lse, dq, dk, dv):
+    dev = q.device
+    _need(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d]")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, q.dtype, dev)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    _need(lse, "lse", torch.float32, dev)
+    if tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("lse must be [T, H]")
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        t = torch.empty_like(q) if t is None else t
+        _need(t, name, q.dtype, dev)
+        outs.append(t)
+    return outs
+
+
+def rr_attn_bwd_run(q, k, v, o, dout, lse, B: int, workspace, scale=None, dq=None, dk=None, dv=None,
+                    stream=None):
+    """Gradients (dq, dk, dv) with the plan in ``workspace``: one from rr_attn_plan in a
+    workspace of rr_attn_bwd_workspace_bytes (``rr_attn_plan(..., backward=True)``)."""
+    dq, dk, dv = _bwd_tensors(q, k, v, o, dout, lse, dq, dk, dv)
+    _need(workspace, "workspace", torch.uint8, q.device)
+    T, H, d = q.shape
+    _check("rr_attn_bwd_run", _lib.rr_attn_bwd_run(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H, d,
+        _rr_dtype(q), float(scale or 0.0), _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
+    return dq, dk, dv
+
+
+def rr_attn_bwd(q, k, v, o, dout, lse, offsets, cand_start, valid=None, attend_padded_history=False,
+                scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Plan and backward in one call: (dq, dk, dv), each [T, H, d] like q."""
+    dq, dk, dv = _bwd_tensors(q, k, v, o, dout, lse, dq, dk, dv)
+    dev = q.device
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if valid is not None:
+        _need(valid, "valid", torch.uint8, dev)
+    T, H, d = q.shape
+    B = offsets.numel() - 1
+    if cand_start.numel() != B:
+        raise ValueError("cand_start must have B entries")
+    ws = _workspace(rr_attn_bwd_workspace_bytes(B, T, H, d), workspace, dev)
+    _check("rr_attn_bwd", _lib.rr_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(offsets), _ptr(cand_start), _ptr(valid), int(bool(attend_padded_history)), B, T, H, d,
+        _rr_dtype(q), float(scale or 0.0), _ptr(ws), ws.numel(), _stream(stream, dev)))
+    return dq, dk, dv
 
 
 def rr_cand_only_plan(hist_offsets, cand_offsets, Th: int, Tc: int, H: int, d: int, dtype,

@@ -14,6 +14,12 @@ definition -- per user and head, P = softmax(scale * q k^T masked by the explici
 Rows that admit no key (segment 0) have P = 0: they get no gradient and give none.
 ``attention_lse`` gives each row's log-sum-exp of its admitted scaled scores (natural
 log), the statistic a backward pass reuses from the forward; -inf for such rows.
+
+``gradient_error_scale`` is not a result of the method: it is the magnitude that
+rounding-error analysis attaches to each gradient element when P and dS are rounded
+to a narrow format before their products and o is stored in that format, so that a
+test can bound a low-precision implementation's error (|err| <= c u (E + |grad|) for
+unit roundoff u).
 """
 from __future__ import annotations
 
@@ -81,3 +87,51 @@ def attention_lse(q, k, offsets, cand_start, valid=None, attend_padded_history=F
             m = s.max(axis=1)
             out[lo:hi, h][has] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
     return out
+
+
+def _user_head_error_scale(q, k, v, do, mask, sc):
+    """One user and head: the error scales (Eq, Ek, Ev) of ``gradient_error_scale``."""
+    s = np.where(mask, sc * (q @ k.T), -np.inf)
+    has = mask.any(axis=1)
+    p = np.zeros_like(s)
+    if has.any():
+        m = s[has].max(axis=1, keepdims=True)
+        e = np.where(mask[has], np.exp(s[has] - m), 0.0)
+        p[has] = e / e.sum(axis=1, keepdims=True)
+    dp = do @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    # rowsum(dO * o) taken from a rounded o: o's own bound is u (|o| + P|v|) <= 2u P|v|
+    dsum = 2.0 * (np.abs(do) * (p @ np.abs(v))).sum(axis=1, keepdims=True)
+    aq, ak = np.abs(q), np.abs(k)
+    eq = sc * (np.abs(ds) @ ak + dsum * (p @ ak))
+    ek = sc * (np.abs(ds).T @ aq + p.T @ (dsum * aq))
+    ev = p.T @ np.abs(do)
+    return eq, ek, ev
+
+
+def gradient_error_scale(q, k, v, do, offsets, cand_start, valid=None, attend_padded_history=False,
+                         scale=None):
+    """Per-element rounding-error scales (Eq, Ek, Ev), float64 [T, H, d] each:
+
+        Eq = scale (|dS| |k| + D (P |k|)),   Ek = scale (|dS|^T |q| + P^T (D |q|)),   Ev = P^T |dO|
+
+    with D_i = 2 sum_e |dO_ie| (P |v|)_ie.  The first terms are the sums of absolute
+    products whose one rounded factor (dS, or P for dv) moves each product by at most u
+    of itself; the D terms carry the error of rowsum(dO * o) when o was rounded.  Every
+    entry is >= |gradient| (triangle inequality) and 0 on segment-0 rows."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64); do = np.asarray(do, np.float64)
+    T, H, d = q.shape
+    sc = _scale(scale, d)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    seg = segment_ids(offsets, cand_start, valid, attend_padded_history)
+    eq, ek, ev = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi == lo:
+            continue
+        mask = isolation_mask(seg[lo:hi])
+        for h in range(H):
+            eq[lo:hi, h], ek[lo:hi, h], ev[lo:hi, h] = _user_head_error_scale(
+                q[lo:hi, h], k[lo:hi, h], v[lo:hi, h], do[lo:hi, h], mask, sc)
+    return eq, ek, ev

@@ -5,8 +5,10 @@ Each ``pin_*`` raises AssertionError when the oracle's gradients disagree with
  * torch autograd through torch's CPU scaled_dot_product_attention in float64, with the
    admitted key sets written here from the plain-language rule (a library routine),
  * exactly rounded log-sum-exp sums (math.fsum) for ``attention_lse``,
- * closed forms (a one-row user; a candidate's own key and value), or
- * the page's isolation invariants carried over to gradients.
+ * closed forms (a one-row user; a candidate's own key and value),
+ * the page's isolation invariants carried over to gradients, or
+ * for ``gradient_error_scale``: the triangle inequality, its equality case, and the
+   error of gradients computed with P, dS and o rounded to bfloat16 by torch.
 They call the oracle through its modules at call time, so tests can plant mistakes.
 """
 from __future__ import annotations
@@ -155,5 +157,57 @@ def pin_isolation_of_gradients():
     assert np.all(dk[others] == 0) and np.all(dv[others] == 0)
 
 
+def _rounded_grads(fb, do, sc):
+    """Gradients with P, o and dS rounded to bfloat16 (torch's rounding) and every other
+    step in float64: the arithmetic ``gradient_error_scale`` bounds."""
+    import torch
+
+    def r(x):
+        return x.to(torch.bfloat16).to(torch.float64)
+    seg = G.segment_ids(fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history)
+    out = [np.zeros(fb.q.shape) for _ in range(3)]
+    for b in range(fb.B):
+        lo, hi = int(fb.offsets[b]), int(fb.offsets[b + 1])
+        rows = range(lo, hi)
+        adm = np.array([[bool(seg[i]) and (seg[j] == 1 or (i == j and seg[i] == -1)) for j in rows]
+                        for i in rows], bool).reshape(hi - lo, hi - lo)
+        m = torch.from_numpy(adm)
+        for h in range(fb.H):
+            q, k, v, g = (torch.from_numpy(np.asarray(x[lo:hi, h], np.float64)) for x in (fb.q, fb.k, fb.v, do))
+            s = (sc * q @ k.T).masked_fill(~m, float("-inf"))
+            p = torch.softmax(s, dim=1).nan_to_num(0.0)
+            o = r(p @ v)
+            ds = r(p * (g @ v.T - (g * o).sum(dim=1, keepdim=True)))
+            out[0][lo:hi, h] = r(sc * ds @ k).numpy()
+            out[1][lo:hi, h] = r(sc * ds.T @ q).numpy()
+            out[2][lo:hi, h] = r(r(p).T @ g).numpy()
+    return out
+
+
+def pin_error_scale():
+    rng = rng_for(95)
+    u = 2.0 ** -8                     # unit roundoff of bfloat16 (8 significant bits)
+    for flag in (False, True):
+        fb = make_full_batch(rng, "err-scale", prefix=[1, 2, 0], hist=[5, 0, 9], cand=[3, 2, 1],
+                             pad=[2, 0, 1], attend_padded_history=flag, H=2, d=8, dtype="f32",
+                             scaled=False)
+        do = rng.standard_normal(fb.q.shape)
+        sc = 1.0 / math.sqrt(fb.d)
+        grads = _grads(fb, do)
+        es = G.gradient_error_scale(fb.q, fb.k, fb.v, do, fb.offsets, fb.cand_start, fb.valid, flag)
+        seg = G.segment_ids(fb.offsets, fb.cand_start, fb.valid, flag)
+        for g, e in zip(grads, es):
+            assert np.all(e >= np.abs(g) * (1 - 1e-12) - 1e-15)      # triangle inequality
+            assert np.all(e[seg == 0] == 0)
+        # equality case: every product of dv = P^T dO has one sign when dO >= 0
+        ev = G.gradient_error_scale(fb.q, fb.k, fb.v, np.abs(do), fb.offsets, fb.cand_start, fb.valid,
+                                    flag)[2]
+        dv = _grads(fb, np.abs(do))[2]
+        assert np.max(np.abs(ev - dv)) <= 1e-12 * max(1.0, float(np.max(ev)))
+        # the scale bounds the error of the rounded computation
+        for g, e, gr in zip(grads, es, _rounded_grads(fb, do, sc)):
+            assert np.all(np.abs(gr - g) <= 1.02 * u * (e + np.abs(g)) + 1e-300)
+
+
 BWD_PINS = [pin_finite_differences, pin_torch_autograd, pin_lse, pin_closed_forms,
-            pin_isolation_of_gradients]
+            pin_isolation_of_gradients, pin_error_scale]

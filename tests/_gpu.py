@@ -79,6 +79,29 @@ def assert_close(got, ref, dtype: str, what: str = ""):
             raise AssertionError(f"{what}: bf16 tolerance exceeded at {i}: got {got[i]} ref {ref[i]}")
 
 
+# bf16 gradients: P and dS enter their products rounded to bf16 and o, dq, dk, dv are
+# stored in bf16 (unit roundoff u = 2^-8), with fp32 accumulation.  Rounding-error
+# analysis bounds each element by u (E + |grad|), E the oracle's gradient_error_scale;
+# the factor 1.25 covers fp32 accumulation over up to 2^14 terms (2^14 * 2^-24 = u / 4)
+# and P's fp32 evaluation (about 1e-6 relative).
+GRAD_U, GRAD_C = 2.0 ** -8, 1.25
+
+
+def assert_close_grad(got, ref, escale, what: str = ""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape == np.shape(escale), (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    if not got.size:
+        return
+    excess = np.abs(got - ref) - GRAD_C * GRAD_U * (np.asarray(escale) + np.abs(ref))
+    worst = float(excess.max())
+    if worst > 0:
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        raise AssertionError(f"{what}: gradient bound exceeded at {i}: got {got[i]} ref {ref[i]} "
+                             f"scale {np.asarray(escale)[i]}")
+
+
 def sample_full_rows(fb, per_user: int, seed: int):
     """Stratified (row, head) samples: every user's first and last row, first and last
     candidate, last history row, plus ``per_user`` random rows, each with a random head."""

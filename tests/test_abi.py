@@ -133,6 +133,43 @@ def test_rope_argument_errors():
     assert lib.rr_rope_positions(None, None, None, 0, 0, None, None) == rr.RR_OK
 
 
+def test_backward_argument_errors():
+    rr, lib = _lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, off=FAKE,
+                 cs=FAKE, B=2, T=10, H=2, d=64, dt=rr.RR_BF16, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.rr_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                               a["off"], a["cs"], None, 0, a["B"], a["T"], a["H"], a["d"], a["dt"], 0.0,
+                               a["ws"], a["ws_bytes"], None)
+    assert call(B=-1) == rr.RR_EINVAL
+    assert call(dt=9) == rr.RR_EDTYPE
+    assert call(dt=rr.RR_F32) == rr.RR_EUNSUPPORTED       # the backward is bf16 only
+    for d in (16, 32, 48):
+        assert call(d=d) == rr.RR_EUNSUPPORTED, d
+    assert call(off=None) == rr.RR_EINVAL
+    assert call(ws=None) == rr.RR_EWORKSPACE
+    need = lib.rr_attn_bwd_workspace_bytes(2, 10, 2, 64)
+    assert need > lib.rr_attn_workspace_bytes(2, 10, 2, 64)   # plus rowsum(dO * o) per row and head
+    assert call(ws_bytes=need - 1) == rr.RR_EWORKSPACE
+    assert lib.rr_attn_bwd_workspace_bytes(2, 10, 2, 32) == 0
+    assert call(B=0, q=None, ws=None) == rr.RR_OK
+    # the run step checks its tensors before any launch
+    run = lib.rr_attn_bwd_run
+    args = [FAKE] * 9 + [2, 10, 2, 64, rr.RR_BF16, 0.0, FAKE, 1 << 30, None]
+    for i in range(9):
+        a = list(args)
+        a[i] = None
+        assert run(*a) == rr.RR_EINVAL, i
+    a = list(args)
+    a[16] = need - 1
+    assert run(*a) == rr.RR_EWORKSPACE
+    # the forward with lse checks like rr_attn_run
+    assert lib.rr_attn_run_lse(None, FAKE, FAKE, FAKE, FAKE, 2, 10, 2, 64, 1, 0.0, FAKE, 1 << 30,
+                               None) == rr.RR_EINVAL
+
+
 def test_workspace_size_grows_with_work():
     _, lib = _lib()
     a = lib.rr_attn_workspace_bytes(64, 16000, 4, 64)

@@ -1,0 +1,173 @@
+"""GPU parity of the backward pass (rr_attn_plan / rr_attn_run_lse / rr_attn_bwd_run and
+rr_attn_bwd) against the float64 oracle's gradients of the same masked attention."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _gpu import assert_close, assert_close_grad, full_dev, gpu, needs_gpu, rr, to_dev, torch_dtype
+from oracle import attention as A
+from oracle import backward as BW
+from oracle.jagged import segment_ids
+
+pytestmark = [gpu, needs_gpu]
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _train_step(fb, do_seed, scale=None, host=True):
+    """Forward with lse, then backward, through the C ABI.  Returns the device tensors (and,
+    with ``host``, float64 host copies of o, lse, dq, dk, dv)."""
+    dv = full_dev(fb)
+    T, H, d = fb.q.shape
+    dout = W.draw_output_grad(do_seed, T, H, d, fb.dtype)
+    dv["dout"] = to_dev(dout, torch_dtype(fb.dtype))
+    ws = rr().rr_attn_plan(dv["offsets"], dv["cand_start"], T, H, d, dv["q"].dtype, dv["valid"],
+                           fb.attend_padded_history, backward=True)
+    o, lse = rr().rr_attn_run_lse(dv["q"], dv["k"], dv["v"], fb.B, ws, scale=scale)
+    dq, dk, dvv = rr().rr_attn_bwd_run(dv["q"], dv["k"], dv["v"], o, dv["dout"], lse, fb.B, ws,
+                                       scale=scale)
+    torch.cuda.synchronize()
+    out = dict(dout=dout, dev=dv, raw=(o, lse, dq, dk, dvv))
+    if host:
+        out.update(o=_np(o), lse=lse.cpu().numpy().astype(np.float64), dq=_np(dq), dk=_np(dk), dv=_np(dvv))
+    return out
+
+
+def _check_grads(fb, got, what, scale=None):
+    args = (fb.q, fb.k, fb.v, got["dout"], fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history,
+            scale)
+    ref = BW.full_attention_backward(*args)
+    es = BW.gradient_error_scale(*args)
+    for name, r, e in zip(("dq", "dk", "dv"), ref, es):
+        assert_close_grad(got[name], r, e, f"{what} {name}")
+    seg = segment_ids(fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history)
+    for name in ("dq", "dk", "dv"):
+        assert not got[name][seg == 0].any(), f"{what} {name}: padding rows not zero"
+
+
+def _batch(name, d, seed, **kw):
+    rng = np.random.default_rng(seed)
+    base = dict(prefix=[4, 2, 0, 3, 1], hist=[300, 0, 45, 700, 129], cand=[37, 5, 0, 128, 1], H=3)
+    base.update(kw)
+    return W.make_full_batch(rng, name, d=d, scaled=False, seed=seed, **base)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_ragged(d):
+    """Users with an empty history, no candidates, one candidate, and tails of every size."""
+    fb = _batch("bwd-ragged", d, 7000 + d)
+    got = _train_step(fb, 7100 + d)
+    _check_grads(fb, got, f"ragged d={d}")
+
+
+@pytest.mark.parametrize("attend", [False, True])
+def test_backward_padding_and_holes(attend):
+    rng = np.random.default_rng(71)
+    fb0 = _batch("bwd-pad", 128, 7200, pad=[0, 3, 20, 0, 64])
+    valid = np.ones(fb0.T, np.uint8) if fb0.valid is None else fb0.valid.copy()
+    valid[rng.choice(fb0.T, 40, replace=False)] = 0      # holes anywhere, candidates included
+    fb = W.FullBatch(**{**fb0.__dict__, "valid": valid, "attend_padded_history": attend})
+    got = _train_step(fb, 7300 + int(attend))
+    _check_grads(fb, got, f"padding attend={attend}")
+
+
+def test_lse_matches_oracle():
+    for fb in (_batch("lse-bf16", 64, 7400, pad=[0, 0, 5, 0, 9]), W.config1()):
+        dv = full_dev(fb)
+        T, H, d = fb.q.shape
+        ws = rr().rr_attn_plan(dv["offsets"], dv["cand_start"], T, H, d, dv["q"].dtype, dv["valid"],
+                               fb.attend_padded_history)
+        o, lse = rr().rr_attn_run_lse(dv["q"], dv["k"], dv["v"], fb.B, ws)
+        o_plain = rr().rr_attn_run(dv["q"], dv["k"], dv["v"], fb.B, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_plain), "the lse output changed o"
+        ref = BW.attention_lse(fb.q, fb.k, fb.offsets, fb.cand_start, fb.valid, fb.attend_padded_history)
+        got = lse.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref)
+        assert np.array_equal(np.isfinite(got), fin) and np.all(got[~fin] == -np.inf)
+        err = np.abs(got[fin] - ref[fin]) - (1e-5 + 2e-6 * np.abs(ref[fin]))
+        assert float(err.max()) <= 0, f"{fb.name}: lse off by {float(np.abs(got[fin] - ref[fin]).max()):.3e}"
+
+
+def test_backward_forward_outputs_and_custom_scale():
+    fb = _batch("bwd-scale", 64, 7500)
+    got = _train_step(fb, 7501, scale=0.05)
+    ref_o = A.full_attention(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, scale=0.05)
+    assert_close(got["o"], ref_o, "bf16", "forward of the backward plan")
+    _check_grads(fb, got, "scale 0.05", scale=0.05)
+
+
+def test_backward_deterministic_and_one_call():
+    fb = _batch("bwd-det", 128, 7600)
+    a = _train_step(fb, 7601)
+    o, lse, dq, dk, dv = a["raw"]
+    d = a["dev"]
+    for _ in range(2):
+        g = rr().rr_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, d["offsets"], d["cand_start"],
+                             d["valid"], fb.attend_padded_history)
+        torch.cuda.synchronize()
+        for x, y, n in zip(g, (dq, dk, dv), ("dq", "dk", "dv")):
+            assert torch.equal(x, y), f"{n} differs between calls"
+
+
+def test_backward_candidate_order():
+    """Permuting one user's candidates permutes every candidate's gradients and every dq
+    bit for bit (each depends on its own row and the user's history only)."""
+    fb = _batch("bwd-perm", 128, 7700)
+    base = _train_step(fb, 7701)
+    b = 3
+    cs, hi = int(fb.cand_start[b]), int(fb.offsets[b + 1])
+    perm = np.arange(fb.T)
+    perm[cs:hi] = cs + np.random.default_rng(5).permutation(hi - cs)
+    fb2 = W.FullBatch(**{**fb.__dict__, "q": fb.q[perm], "k": fb.k[perm], "v": fb.v[perm]})
+    dout = base["dout"][perm]
+    dv = full_dev(fb2)
+    dv["dout"] = to_dev(dout, torch.bfloat16)
+    T, H, d = fb2.q.shape
+    ws = rr().rr_attn_plan(dv["offsets"], dv["cand_start"], T, H, d, torch.bfloat16, backward=True)
+    o, lse = rr().rr_attn_run_lse(dv["q"], dv["k"], dv["v"], fb2.B, ws)
+    g = rr().rr_attn_bwd_run(dv["q"], dv["k"], dv["v"], o, dv["dout"], lse, fb2.B, ws)
+    torch.cuda.synchronize()
+    dq2, dk2, dv2 = (_np(x) for x in g)
+    assert np.array_equal(dq2, base["dq"][perm]), "dq changed with candidate order"
+    cand = np.zeros(fb.T, bool)
+    for u in range(fb.B):
+        cand[int(fb.cand_start[u]):int(fb.offsets[u + 1])] = True
+    assert np.array_equal(dk2[cand], base["dk"][perm][cand])
+    assert np.array_equal(dv2[cand], base["dv"][perm][cand])
+
+
+def _one_user(fb, b, h, dout):
+    """User b, head h of a batch as a one-user, one-head batch for the oracle: its
+    gradients and their error scales."""
+    lo, hi = int(fb.offsets[b]), int(fb.offsets[b + 1])
+    sl = slice(lo, hi)
+    valid = None if fb.valid is None else fb.valid[sl]
+    args = (fb.q[sl, h:h + 1], fb.k[sl, h:h + 1], fb.v[sl, h:h + 1], dout[sl, h:h + 1],
+            np.array([0, hi - lo], np.int32), np.array([int(fb.cand_start[b]) - lo], np.int32), valid,
+            fb.attend_padded_history)
+    return BW.full_attention_backward(*args), BW.gradient_error_scale(*args)
+
+
+@pytest.mark.parametrize("cfg", [3, 6])
+def test_backward_full_size_sampled_users(cfg):
+    """The lognormal-history batch (d=64) and the padded skew batch (d=128) at full size; the
+    oracle checks whole users (every row, one head each): the shortest, median and longest
+    history."""
+    fb = W.make_config(cfg)
+    got = _train_step(fb, 7800 + cfg, host=False)
+    _, _, dq, dk, dv = got["raw"]
+    order = np.argsort(fb.hist, kind="stable")
+    picks = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    rng = np.random.default_rng(cfg)
+    for b in picks:
+        lo, hi = int(fb.offsets[b]), int(fb.offsets[b + 1])
+        h = int(rng.integers(0, fb.H))
+        ref, es = _one_user(fb, b, h, got["dout"])
+        for name, t, r, e in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, es):
+            assert_close_grad(_np(t[lo:hi, h:h + 1]), r, e, f"config {cfg} user {b} head {h} {name}")

@@ -226,6 +226,13 @@ def make_cand_only_batch(rng, name, hist, cand, H, d, dtype="bf16", scaled=True,
                          seed=seed, meta=dict(meta or {}))
 
 
+def draw_output_grad(seed: int, T: int, H: int, d: int, dtype: str = "bf16",
+                     scaled: bool = False) -> np.ndarray:
+    """An upstream gradient dO [T, H, d] for the backward pass: N(0, 1) entries (N(0, 1/d) when
+    ``scaled``), rounded to bf16 for bf16 batches; stream 3 of ``seed``."""
+    return _draw(int(seed), 3, T, H, d, scaled, dtype)
+
+
 def split_to_cand_only(fb: FullBatch) -> CandOnlyBatch:
     """Re-express a full batch without padding as candidate-only inputs.
 
