@@ -11,6 +11,11 @@ inputs (>= 1 GiB in total) that no step finds its data in the 256 MB Infinity Ca
 
 metric: effective (non-pad) attention TFLOP/s = 4 * d * H * sum_b [n_b^2 + c_b (n_b + 1)]
 per step / step time; candidates/s is reported beside it.
+
+``--backward`` (full-sequence bf16 workloads) makes a step one training pass of the
+attention: plan, forward with the log-sum-exp (``rr_attn_run_lse``) and the backward
+(``rr_attn_bwd_run``: dq, dk, dv).  The backward counts 2.5x the forward's effective
+FLOPs (five products of the forward's size against the forward's two).
 """
 from __future__ import annotations
 
@@ -42,6 +47,8 @@ def parse_args():
     p.add_argument("--rope", action="store_true",
                    help="rotate q and k at right-anchored positions (rr_rope_qk) inside every step, "
                         "before the attention")
+    p.add_argument("--backward", action="store_true",
+                   help="a step is plan + forward with lse + backward (full-sequence bf16, d 64 or 128)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -131,9 +138,10 @@ def work_counts(cfg, b):
             acc.full_mode_bytes(b.T, b.H, b.d, es), int(b.cand.sum()))
 
 
-def gpu_setup(cfg, b, torch, rr, rope=False):
+def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
     """Device copies of the inputs (rotated), outputs, the workspace and the step calls:
-    plan(), run(i) (with the rotary encoding first when ``rope``) and rope_only(i)."""
+    plan(), run(i) (with the rotary encoding first when ``rope``; forward with lse and then
+    the backward when ``backward``), rope_only(i) and bwd_only(i)."""
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if b.dtype == "bf16" else torch.float32
 
@@ -149,17 +157,26 @@ def gpu_setup(cfg, b, torch, rr, rope=False):
         ws = torch.empty(rr.rr_cand_only_workspace_bytes(b.B, Th, Tc, H, d), dtype=torch.uint8, device=dev)
     else:
         base = [up(b.q, dt), up(b.k, dt), up(b.v, dt)]
+        if backward:
+            import workloads as W
+            base.append(up(W.draw_output_grad(b.seed + 77, b.T, b.H, b.d, b.dtype), dt))
         off, cst = up(b.offsets), up(b.cand_start)
         valid = None if b.valid is None else up(b.valid)
         out_like = base[0]
-        ws = torch.empty(rr.rr_attn_workspace_bytes(b.B, b.T, b.H, b.d), dtype=torch.uint8, device=dev)
-    footprint = sum(t.numel() * t.element_size() for t in base) + out_like.numel() * out_like.element_size()
+        nbytes = (rr.rr_attn_bwd_workspace_bytes if backward else rr.rr_attn_workspace_bytes)(b.B, b.T, b.H, b.d)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    n_out = 4 if backward else 1          # o (and dq, dk, dv)
+    footprint = (sum(t.numel() * t.element_size() for t in base) +
+                 n_out * out_like.numel() * out_like.element_size())
     copies = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
     sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
     outs = [torch.empty_like(out_like) for _ in range(copies)]
+    grads = [[torch.empty_like(out_like) for _ in range(3)] for _ in range(copies)] if backward else None
+    lse = torch.empty((b.T, b.H), dtype=torch.float32, device=dev) if backward else None
 
     # rotary q / k land in one set of buffers that the attention of the same step reads
     rot = [torch.empty_like(t) for t in base] if rope else None
+    bwd_only = None
     if cfg == 4:
         hist_len = (hoff[1:] - hoff[:-1]).contiguous()
         hist_end, cand_first = hoff[1:].contiguous(), coff[:-1].contiguous()
@@ -188,23 +205,40 @@ def gpu_setup(cfg, b, torch, rr, rope=False):
             s = sets[i % copies]
             rr.rr_rope_qk(s[0], s[1], off, cst, q_out=rot[0], k_out=rot[1])
 
+        def bwd_only(i):
+            s, g = sets[i % copies], grads[i % copies]
+            rr.rr_attn_bwd_run(s[0], s[1], s[2], outs[i % copies], s[3], lse, b.B, ws, dq=g[0], dk=g[1],
+                               dv=g[2])
+
         def run(i):
             s = sets[i % copies]
             if rope:
                 rope_only(i)
                 rr.rr_attn_run(rot[0], rot[1], s[2], b.B, ws, out=outs[i % copies])
+            elif backward:
+                rr.rr_attn_run_lse(s[0], s[1], s[2], b.B, ws, out=outs[i % copies], lse=lse)
+                bwd_only(i)
             else:
                 rr.rr_attn_run(s[0], s[1], s[2], b.B, ws, out=outs[i % copies])
-    return plan, run, rope_only, copies, footprint
+    return plan, run, rope_only, bwd_only, copies, footprint
 
 
-def cpu_baseline(cfg, b, budget_s, rope=False):
+def cpu_baseline(cfg, b, budget_s, rope=False, backward=False):
     """The oracle, as it stands, on the host cores: whole batches (or the first users of one)
-    repeated until about ``budget_s`` of CPU time; effective TFLOP/s of what it finished."""
+    repeated until about ``budget_s`` of CPU time; effective TFLOP/s of what it finished
+    (forward and backward FLOPs when ``backward``: the forward oracle, then the gradients)."""
     import numpy as np
     from oracle import attention as A
+    from oracle import backward as BW
     from oracle import rotary as RO
     full_fn = RO.full_attention_rope if rope else A.full_attention
+    if backward:
+        import workloads as W
+        dout = W.draw_output_grad(b.seed + 77, b.T, b.H, b.d, b.dtype)
+
+        def full_fn(q, k, v, offsets, cand_start, valid, flag, rows=slice(None)):
+            A.full_attention(q, k, v, offsets, cand_start, valid, flag)
+            BW.full_attention_backward(q, k, v, dout[rows], offsets, cand_start, valid, flag)
     cand_fn = RO.cand_only_attention_rope if rope else A.cand_only_attention
     try:
         from threadpoolctl import threadpool_info
@@ -244,16 +278,19 @@ def cpu_baseline(cfg, b, budget_s, rope=False):
                 lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
                 sl = slice(lo, hi)
                 valid = None if b.valid is None else b.valid[sl]
+                extra = {"rows": sl} if backward else {}
                 full_fn(b.q[sl], b.k[sl], b.v[sl], [0, hi - lo], [int(b.cand_start[u]) - lo],
-                                 valid, b.attend_padded_history)
+                        valid, b.attend_padded_history, **extra)
                 e, _ = acc.full_mode_counts(b.prefix[u:u + 1], b.hist[u:u + 1], b.cand[u:u + 1],
                                             b.pad[u:u + 1], b.attend_padded_history)
                 done_flops += acc.attention_flops(e, b.H, b.d)
                 done_cands += int(b.cand[u])
                 users += 1
         sample = ((f"whole batch x{reps}" if small else f"first {users} of {b.B} users") + ", float64 oracle"
-                  + (" with rotary q/k" if rope else ""))
+                  + (" with rotary q/k" if rope else "") + (", forward + backward" if backward else ""))
     dt = time.perf_counter() - t0
+    if backward:
+        done_flops *= 3.5                 # forward + backward (2.5x), as the GPU figure counts
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2), "candidates_per_s": done_cands / dt}
 
@@ -273,8 +310,16 @@ def main():
         return
     cfg = args.config
     b = make_batch(cfg)
+    if args.backward and (cfg == 4 or b.dtype != "bf16" or b.d not in (64, 128) or args.rope):
+        print("--backward runs the full-sequence bf16 workloads with d 64 or 128 (configs 2, 3, 5, 6, 7), "
+              "without --rope", file=sys.stderr)
+        sys.exit(2)
     eff_flops, exec_flops, alg_bytes, n_cands = work_counts(cfg, b)
-    plan, run, rope_only, copies, footprint = gpu_setup(cfg, b, torch, rr, rope=args.rope)
+    fwd_eff, fwd_exec = eff_flops, exec_flops
+    if args.backward:       # a training step: forward + backward (2.5x the forward)
+        eff_flops, exec_flops = 3.5 * eff_flops, 3.5 * exec_flops
+    plan, run, rope_only, bwd_only, copies, footprint = gpu_setup(cfg, b, torch, rr, rope=args.rope,
+                                                                  backward=args.backward)
     torch.cuda.synchronize()
 
     # size the run to about a second of GPU work unless told otherwise
@@ -353,8 +398,14 @@ def main():
     if args.rope:
         rope_ms = time_launches(rope_only)
         kernel_ms = time_launches(run) - rope_ms     # the attention of the rotary step
+    elif args.backward:
+        bwd_ms = time_launches(bwd_only)
+        kernel_ms = time_launches(run) - bwd_ms      # the forward of the training step
     else:
         kernel_ms = time_launches(run)
+    # the roofline entry covers the forward kernel
+    eff_flops_all, exec_flops_all = eff_flops, exec_flops
+    eff_flops, exec_flops = fwd_eff, fwd_exec
 
     flop_per_byte = eff_flops / alg_bytes
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -380,8 +431,8 @@ def main():
         "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
         "config": dict(describe(cfg, b), parallelism="none (1 GPU)"),
         "candidates_per_s": n_cands / (ms_per_step / 1e3),
-        "effective_flops_per_step": eff_flops, "executed_flops_per_step": exec_flops,
-        "executed_tflops": exec_flops / (ms_per_step / 1e3) / 1e12,
+        "effective_flops_per_step": eff_flops_all, "executed_flops_per_step": exec_flops_all,
+        "executed_tflops": exec_flops_all / (ms_per_step / 1e3) / 1e12,
         "input_copies_rotated": copies, "footprint_bytes": footprint,
         "timing": "hip graph replay" if graph is not None else "eager launches",
         "roofline": roof,
@@ -395,8 +446,15 @@ def main():
                        "unit": "GB/s", "frac": rope_bytes / (rope_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                        "alg_bytes": rope_bytes}
         out["config"]["rope"] = "right-anchored rotary q/k, base 10000, inside every step"
+    if args.backward:
+        bwd_flops = 2.5 * fwd_exec
+        out["backward"] = {"kernels": ["k_bwd_dq", "k_bwd_dkdv"], "kernel_ms": bwd_ms, "bound": "mfma",
+                           "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                           "alg_flops": bwd_flops}
+        out["config"]["step"] = "plan + forward with lse + backward (dq, dk, dv)"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, b, args.cpu_seconds, rope=args.rope)
+        out["cpu_baseline"] = cpu_baseline(cfg, b, args.cpu_seconds, rope=args.rope, backward=args.backward)
     print(json.dumps(out), flush=True)
 
 
