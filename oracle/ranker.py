@@ -1,0 +1,133 @@
+"""Oracle: the ranker's layer stack over a jagged batch, in float64 (test infrastructure only).
+
+Candidate isolation attention mask page, section "只更新候选的末尾层": the first
+L - N layers run over the whole sequence [prefix | history | candidates] under the
+isolation mask; then the hidden states are split into history and candidates, the
+history states are frozen, and the last N layers update only the candidates, whose
+queries read the frozen history (as keys and values) and their own key and value.
+Section "位置编码：候选共用一个位置" places the rotary positions.  Because the history
+never reads candidates (section "掩码长什么样"), the history's keys and values of
+every layer are the same for any set of candidates: a later request for the same
+users with new candidates can reuse them, and every layer then becomes a
+candidate-only layer over that cache.
+
+The pages do not print the layer's inside.  The reading taken here (each listed in
+the design notes): a pre-norm attention block,
+
+    h = rms_norm(x) * gain,   [q | k | v] = h W_qkv^T,   q, k <- rotary(q, k)
+    x <- x + attention(q, k, v) W_o^T
+
+with W_qkv [3D, D], W_o [D, D] (out x in), D = H d, heads laid out [H, d] inside a
+row, rms_norm(x) = x / sqrt(mean(x^2) + eps), eps = 1e-6.  A frozen history row of a
+candidate-only layer gives its key and value through that layer's own norm and
+projections (and its rotary position).  No feed-forward block and no action head.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .attention import cand_only_attention, full_attention
+from .rotary import DEFAULT_BASE, right_anchored_positions, rope
+
+RMS_EPS = 1e-6
+
+
+@dataclass
+class Layer:
+    gain: np.ndarray      # [D]
+    w_qkv: np.ndarray     # [3D, D]
+    w_o: np.ndarray       # [D, D]
+
+
+def rms_norm(x, gain, eps=RMS_EPS) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain over the last axis; float64."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(gain, np.float64)
+
+
+def _qkv(x, layer, H, d):
+    h = rms_norm(x, layer.gain)
+    qkv = h @ np.asarray(layer.w_qkv, np.float64).T
+    D = H * d
+    return (qkv[:, :D].reshape(-1, H, d), qkv[:, D:2 * D].reshape(-1, H, d),
+            qkv[:, 2 * D:].reshape(-1, H, d))
+
+
+def _out(x, o, layer):
+    return np.asarray(x, np.float64) + o.reshape(o.shape[0], -1) @ np.asarray(layer.w_o, np.float64).T
+
+
+def block_full(x, layer, offsets, cand_start, H, d, base=DEFAULT_BASE, scale=None) -> np.ndarray:
+    """One full-sequence layer over x [T, D]; returns the new x."""
+    q, k, v = _qkv(x, layer, H, d)
+    pos = right_anchored_positions(offsets, cand_start)
+    o = full_attention(rope(q, pos, base), rope(k, pos, base), v, offsets, cand_start, scale=scale)
+    return _out(x, o, layer)
+
+
+def history_kv(x_hist, layer, hist_offsets, H, d, base=DEFAULT_BASE):
+    """Keys (rotated at positions 0 .. h_b-1) and values of frozen history rows [Th, D]."""
+    _, k, v = _qkv(x_hist, layer, H, d)
+    hoff = np.asarray(hist_offsets, np.int64)
+    return rope(k, right_anchored_positions(hoff, hoff[1:]), base), v
+
+
+def block_cand_only(x_cand, k_hist, v_hist, layer, hist_offsets, cand_offsets, H, d, base=DEFAULT_BASE,
+                    scale=None) -> np.ndarray:
+    """One candidate-only layer: candidates [Tc, D] read the user's history keys (already
+    rotated) and values [Th, H, d] plus their own; returns the new candidate states."""
+    q, k, v = _qkv(x_cand, layer, H, d)
+    hoff = np.asarray(hist_offsets, np.int64)
+    coff = np.asarray(cand_offsets, np.int64)
+    pos = right_anchored_positions(coff, coff[:-1], pos_base=np.diff(hoff))
+    o = cand_only_attention(rope(q, pos, base), k_hist, v_hist, rope(k, pos, base), v, hoff, coff, scale)
+    return _out(x_cand, o, layer)
+
+
+def split_history_and_candidates(x, offsets, cand_start):
+    """(x_hist [Th, D], x_cand [Tc, D], hist_offsets, cand_offsets): each user's rows before
+    its candidate start, then its candidate rows, both concatenated in user order."""
+    offsets = np.asarray(offsets, np.int64)
+    cand_start = np.asarray(cand_start, np.int64)
+    hist_rows = [np.arange(offsets[b], cand_start[b]) for b in range(len(cand_start))]
+    cand_rows = [np.arange(cand_start[b], offsets[b + 1]) for b in range(len(cand_start))]
+    hoff = np.concatenate([[0], np.cumsum([len(r) for r in hist_rows])]).astype(np.int64)
+    coff = np.concatenate([[0], np.cumsum([len(r) for r in cand_rows])]).astype(np.int64)
+    hidx = np.concatenate(hist_rows + [np.zeros(0, np.int64)]).astype(np.int64)
+    cidx = np.concatenate(cand_rows + [np.zeros(0, np.int64)]).astype(np.int64)
+    x = np.asarray(x, np.float64)
+    return x[hidx], x[cidx], hoff, coff
+
+
+def ranker_forward(x, layers, n_cand_only, offsets, cand_start, H, d, base=DEFAULT_BASE, scale=None):
+    """The layer stack over x [T, D]: len(layers) - n_cand_only full layers, the split, then
+    n_cand_only candidate-only layers.  Returns (x_cand [Tc, D], x_hist [Th, D] (frozen),
+    cache): cache[l] = (k_hist, v_hist) of layer l for the history rows, the keys and values
+    a later request reuses."""
+    n_full = len(layers) - n_cand_only
+    cache = []
+    for layer in layers[:n_full]:
+        _, k, v = _qkv(x, layer, H, d)
+        pos = right_anchored_positions(offsets, cand_start)
+        kh = split_history_and_candidates(rope(k, pos, base).reshape(len(x), -1), offsets, cand_start)[0]
+        vh = split_history_and_candidates(v.reshape(len(x), -1), offsets, cand_start)[0]
+        cache.append((kh.reshape(-1, H, d), vh.reshape(-1, H, d)))
+        x = block_full(x, layer, offsets, cand_start, H, d, base, scale)
+    x_hist, x_cand, hoff, coff = split_history_and_candidates(x, offsets, cand_start)
+    for layer in layers[n_full:]:
+        kh, vh = history_kv(x_hist, layer, hoff, H, d, base)
+        cache.append((kh, vh))
+        x_cand = block_cand_only(x_cand, kh, vh, layer, hoff, coff, H, d, base, scale)
+    return x_cand, x_hist, cache
+
+
+def ranker_forward_cached(x_cand, cache, layers, hist_offsets, cand_offsets, H, d, base=DEFAULT_BASE,
+                          scale=None) -> np.ndarray:
+    """Candidates [Tc, D] of a request whose users' history keys and values per layer are in
+    ``cache``: every layer is a candidate-only layer over the cache."""
+    x = np.asarray(x_cand, np.float64)
+    for layer, (kh, vh) in zip(layers, cache):
+        x = block_cand_only(x, kh, vh, layer, hist_offsets, cand_offsets, H, d, base, scale)
+    return x

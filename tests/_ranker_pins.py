@@ -1,0 +1,161 @@
+"""Pins for the layer-stack oracle (oracle/ranker.py).
+
+Each ``pin_*`` raises AssertionError when the oracle disagrees with
+ * torch's CPU ``rms_norm`` in float64 (a library routine) and the closed form of a
+   constant row,
+ * a separate float64 torch implementation of the whole stack: torch's ``linear``,
+   ``rms_norm`` and ``scaled_dot_product_attention`` with the admitted keys written here
+   from the plain-language rule, rotary positions from the page's rule and the rotation
+   as complex multiplication, and the candidate-only layers done the page's fallback
+   way (the full layer over the whole sequence, then the non-candidate rows put back to
+   their frozen states),
+ * closed forms (W_o = 0 leaves every state unchanged; W_q = W_k = 0 with W_v = W_o = I
+   gives each row the mean of its admitted normalised rows), or
+ * the page's invariants: candidate order, history independence, and the cached request
+   (every layer candidate-only over the history keys and values) equal to the full one.
+They call the oracle through its module at call time, so tests can plant mistakes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import ranker as RK
+
+SHAPES = dict(prefix=[1, 0, 2, 1], hist=[3, 0, 4, 6], cand=[2, 3, 0, 4])
+
+
+def _layout(prefix, hist, cand):
+    lengths = np.asarray(prefix) + np.asarray(hist) + np.asarray(cand)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    cand_start = offsets[:-1] + np.asarray(prefix) + np.asarray(hist)
+    return offsets, cand_start
+
+
+def make_stack(seed, n_layers=3, H=2, d=4, shapes=SHAPES):
+    rng = np.random.default_rng(seed)
+    offsets, cand_start = _layout(**shapes)
+    D = H * d
+    x = rng.standard_normal((int(offsets[-1]), D))
+    layers = [RK.Layer(gain=1.0 + 0.2 * rng.standard_normal(D),
+                       w_qkv=rng.standard_normal((3 * D, D)) / np.sqrt(D),
+                       w_o=rng.standard_normal((D, D)) / np.sqrt(D)) for _ in range(n_layers)]
+    return x, layers, offsets, cand_start, H, d
+
+
+def _torch_stack(x, layers, n_cand_only, offsets, cand_start, H, d, base):
+    import torch
+    import torch.nn.functional as F
+    T, D = x.shape
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    pos = torch.zeros(T, dtype=torch.float64)
+    is_hist = torch.zeros(T, dtype=torch.bool)
+    users = []
+    for b in range(len(cand_start)):
+        lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        for r in range(lo, hi):
+            pos[r] = min(r, cs) - lo          # newest history row at cs-1-lo, candidates at cs-lo
+            is_hist[r] = r < cs
+        # a row reads the rows before the candidate start, and a candidate also itself
+        m = torch.tensor([[j < cs - lo or i == j for j in range(hi - lo)] for i in range(hi - lo)],
+                         dtype=torch.bool).reshape(hi - lo, hi - lo)
+        users.append((lo, hi, m))
+    inv = base ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    rot = torch.polar(torch.ones(T, d // 2, dtype=torch.float64), pos[:, None] * inv[None, :])
+
+    def rotate(t):
+        c = torch.view_as_complex(t.reshape(T, H, d // 2, 2).contiguous())
+        return torch.view_as_real(c * rot[:, None, :]).reshape(T, H, d)
+
+    def layer(X, L):
+        h = F.rms_norm(X, (D,), weight=torch.from_numpy(L.gain), eps=RK.RMS_EPS)
+        q, k, v = F.linear(h, torch.from_numpy(L.w_qkv)).split(D, dim=1)
+        q, k, v = rotate(q.reshape(T, H, d)), rotate(k.reshape(T, H, d)), v.reshape(T, H, d)
+        out = torch.zeros(T, H, d, dtype=torch.float64)
+        for lo, hi, m in users:
+            if hi > lo:
+                o = F.scaled_dot_product_attention(q[lo:hi].transpose(0, 1), k[lo:hi].transpose(0, 1),
+                                                   v[lo:hi].transpose(0, 1), attn_mask=m)
+                out[lo:hi] = o.transpose(0, 1)
+        return X + F.linear(out.reshape(T, D), torch.from_numpy(L.w_o))
+
+    n_full = len(layers) - n_cand_only
+    for L in layers[:n_full]:
+        X = layer(X, L)
+    frozen = X.clone()
+    for L in layers[n_full:]:
+        X = torch.where(is_hist[:, None], frozen, layer(X, L))
+    return X[~is_hist].numpy(), frozen[is_hist].numpy()
+
+
+def pin_rms_norm():
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 12)) * rng.uniform(0.01, 10, (7, 1))
+    g = rng.standard_normal(12)
+    want = F.rms_norm(torch.from_numpy(x), (12,), weight=torch.from_numpy(g), eps=RK.RMS_EPS).numpy()
+    assert np.max(np.abs(RK.rms_norm(x, g) - want)) <= 1e-12
+    c = np.full((1, 5), -3.0)
+    assert np.allclose(RK.rms_norm(c, np.arange(5.0)), -3.0 / np.sqrt(9.0 + RK.RMS_EPS) * np.arange(5.0),
+                       rtol=0, atol=1e-15)
+
+
+def pin_torch_stack():
+    for seed, n_cand_only in ((11, 1), (12, 2), (13, 0)):
+        x, layers, off, cs, H, d = make_stack(seed)
+        got_c, got_h, _ = RK.ranker_forward(x, layers, n_cand_only, off, cs, H, d, base=50.0)
+        want_c, want_h = _torch_stack(x, layers, n_cand_only, off, cs, H, d, base=50.0)
+        assert np.max(np.abs(got_c - want_c)) <= 1e-10, seed
+        assert np.max(np.abs(got_h - want_h)) <= 1e-10, seed
+
+
+def pin_closed_forms():
+    x, layers, off, cs, H, d = make_stack(21)
+    D = H * d
+    # W_o = 0: every layer is the identity on the states
+    flat = [RK.Layer(L.gain, L.w_qkv, np.zeros((D, D))) for L in layers]
+    xc, xh, _ = RK.ranker_forward(x, flat, 1, off, cs, H, d)
+    hist = np.concatenate([np.arange(off[b], cs[b]) for b in range(len(cs))]).astype(int)
+    cand = np.concatenate([np.arange(cs[b], off[b + 1]) for b in range(len(cs))]).astype(int)
+    assert np.array_equal(xc, x[cand]) and np.array_equal(xh, x[hist])
+    # W_q = W_k = 0, W_v = W_o = I: one layer adds the mean of the admitted normalised rows
+    w = np.zeros((3 * D, D))
+    w[2 * D:] = np.eye(D)
+    L = RK.Layer(layers[0].gain, w, np.eye(D))
+    got = RK.block_full(x, L, off, cs, H, d)
+    h = RK.rms_norm(x, L.gain)
+    for b in range(len(cs)):
+        lo, c, hi = int(off[b]), int(cs[b]), int(off[b + 1])
+        for r in range(lo, hi):
+            keys = list(range(lo, c)) + ([r] if r >= c else [])
+            assert np.max(np.abs(got[r] - (x[r] + h[keys].mean(axis=0)))) <= 1e-12
+
+
+def pin_invariants():
+    x, layers, off, cs, H, d = make_stack(31)
+    xc, xh, cache = RK.ranker_forward(x, layers, 1, off, cs, H, d)
+    xh0, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    # a later request with the same users: every layer candidate-only over the cache
+    again = RK.ranker_forward_cached(xc0, cache, layers, hoff, coff, H, d)
+    assert np.max(np.abs(again - xc)) <= 1e-12
+    # candidates in another order: the same per-candidate outputs
+    b = 3
+    perm = np.arange(len(x))
+    perm[int(cs[b]):int(off[b + 1])] = np.random.default_rng(5).permutation(
+        np.arange(int(cs[b]), int(off[b + 1])))
+    xc2, xh2, _ = RK.ranker_forward(x[perm], layers, 1, off, cs, H, d)
+    inv = np.argsort(perm[int(cs[b]):int(off[b + 1])] - int(cs[b]))
+    c0 = int(coff[b])
+    assert np.max(np.abs(xc2[c0:c0 + len(inv)][inv] - xc[c0:c0 + len(inv)])) <= 1e-12
+    assert np.array_equal(np.delete(xc2, np.s_[c0:c0 + len(inv)], 0), np.delete(xc, np.s_[c0:c0 + len(inv)], 0))
+    # other candidates change nothing of the history (states or cache) nor of other candidates
+    x3 = x.copy()
+    x3[int(cs[0])] += 5.0
+    xc3, xh3, cache3 = RK.ranker_forward(x3, layers, 1, off, cs, H, d)
+    assert np.array_equal(xh3, xh)
+    for (k1, v1), (k2, v2) in zip(cache, cache3):
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    assert np.array_equal(xc3[1:], xc[1:])
+
+
+RANKER_PINS = [pin_rms_norm, pin_torch_stack, pin_closed_forms, pin_invariants]
