@@ -254,6 +254,90 @@ int rr_rope_qk(const void* q, const void* k, void* q_out, void* k_out, const int
                int32_t d, int dtype, float theta_base, hipStream_t stream);
 
 /*
+ * The ranker's layer stack (Candidate isolation attention mask page, section
+ * "只更新候选的末尾层"): the first n_layers - n_cand_only layers run over the whole
+ * sequence under the isolation mask; then the hidden states split into history
+ * (frozen from here on) and candidates, and the last n_cand_only layers update only
+ * the candidates, whose queries read the frozen history's keys and values and their
+ * own.  Rotary positions are right-anchored (section "位置编码：候选共用一个位置").
+ *
+ * The pages do not print the layer's inside.  Each layer is read as a pre-norm
+ * attention block with the caller's weights:
+ *   h = x / sqrt(mean(x^2) + 1e-6) * norm_gain;  [q | k | v] = h W_qkv^T (bf16);
+ *   q, k rotated (base theta_base, <= 0 selects 10000);  x += attention(q, k, v) W_o^T.
+ * A frozen history row gives a candidate-only layer its key and value through that
+ * layer's norm and projections.  No feed-forward block or action head.
+ *
+ * x (the residual stream) is float32 [rows][D], D = H d, head h of a row at columns
+ * h d .. h d + d - 1.  Supported: d in {32, 64, 128}, D a multiple of 128 (<= 16384);
+ * the attention runs in bf16 with its default scale 1/sqrt(d).  Every kernel computes
+ * a row from that row alone in a fixed order, so a candidate's result does not depend
+ * on the other rows of the batch.
+ */
+typedef struct {
+  const float* norm_gain;  /* float [D], device */
+  const void* w_qkv;       /* bf16 [3D][D] (out x in), device: rows 0..D-1 give q, D..2D-1 k, 2D.. v */
+  const void* w_o;         /* bf16 [D][D] (out x in), device */
+} rr_layer;
+
+/* out = bf16(x / sqrt(mean(x^2) + eps) * gain) per row; x float [M][D], D % 4 == 0; eps <= 0 -> 1e-6. */
+int rr_rms_norm(const float* x, const float* gain, void* out, int32_t M, int32_t D, float eps,
+                hipStream_t stream);
+
+/*
+ * rr_linear -- C = A W^T on the matrix cores: A bf16 [M][K], W bf16 [N][K]; exactly one of
+ * out (bf16 [M][N], written) and residual (float [M][N], residual += C) is given.
+ * N % 128 == 0 and K % 64 == 0 (else RR_EUNSUPPORTED); fp32 accumulation in a fixed order.
+ */
+int rr_linear(const void* a, const void* w, void* out, float* residual, int32_t M, int32_t N, int32_t K,
+              hipStream_t stream);
+
+/* Bytes of workspace rr_ranker_fwd needs (0 on unsupported sizes). */
+size_t rr_ranker_workspace_bytes(int32_t B, int32_t T, int32_t Tc, int32_t H, int32_t d);
+
+/*
+ * rr_ranker_fwd -- one request: the whole stack over a jagged batch (no padding mask).
+ *
+ * x           float [T][D] device: the input states; the full layers update it in place,
+ *             so afterwards it holds the states after the last full layer
+ * layers      HOST array of n_layers rr_layer (device pointers inside)
+ * n_cand_only the last n_cand_only layers are candidate-only (0 <= n_cand_only <= n_layers)
+ * offsets, cand_start  as rr_attn_fwd; Tc = total candidate rows (sum of offsets[b+1] -
+ *             cand_start[b]), the caller's count; Th = T - Tc history rows
+ * x_cand_out  float [Tc][D] device, written: the candidates' final states, users in order
+ * x_hist_out  float [Th][D] device or NULL: the frozen history states (rows before each
+ *             user's candidate start, users in order)
+ * kv_cache    bf16 [n_layers][2][Th][H][d] device or NULL: written with every layer's
+ *             history keys (rotated) and values, for rr_ranker_cached_fwd
+ * workspace   rr_ranker_workspace_bytes(B, T, Tc, H, d) bytes
+ */
+int rr_ranker_fwd(float* x, const rr_layer* layers, int32_t n_layers, int32_t n_cand_only,
+                  const int32_t* offsets, const int32_t* cand_start, int32_t B, int32_t T, int32_t Tc,
+                  int32_t H, int32_t d, float theta_base, float* x_cand_out, float* x_hist_out,
+                  void* kv_cache, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace rr_ranker_cached_fwd needs (0 on unsupported sizes). */
+size_t rr_ranker_cached_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d);
+
+/*
+ * rr_ranker_cached_fwd -- a later request for the same users with new candidates.  The
+ * history never reads candidates (section "掩码长什么样"), so its keys and values of
+ * every layer are those rr_ranker_fwd left in kv_cache, and every layer becomes a
+ * candidate-only layer over them.  The candidates' final states equal, bit for bit, those
+ * rr_ranker_fwd gives the same candidates with the same users.
+ *
+ * x_cand       float [Tc][D] device: the candidates' input states, updated in place to
+ *              their final states
+ * kv_cache     bf16 [n_layers][2][Th][H][d] device, from rr_ranker_fwd
+ * hist_offsets int32 [B+1] into the cache's rows; cand_offsets int32 [B+1] into x_cand
+ * workspace    rr_ranker_cached_workspace_bytes(B, Th, Tc, H, d) bytes
+ */
+int rr_ranker_cached_fwd(float* x_cand, const rr_layer* layers, int32_t n_layers, const void* kv_cache,
+                         const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B, int32_t Th,
+                         int32_t Tc, int32_t H, int32_t d, float theta_base, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * rr_validate_jagged -- debug check of the data contract (HSTU scaling notes, section
  * "手算 padding 的浪费与 offset": empty sequences, offset type and user boundaries need
  * checking).  ORs bits into *err_flags (device int32, caller zeroes it first):

@@ -45,6 +45,14 @@ _SIGS = {
                                        ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "rr_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I, _I,
                                    _I, _I, ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_rms_norm": (ctypes.c_int, [_P, _P, _P, _I, _I, ctypes.c_float, _P]),
+    "rr_linear": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P]),
+    "rr_ranker_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "rr_ranker_fwd": (ctypes.c_int, [_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P,
+                                     _P, ctypes.c_size_t, _P]),
+    "rr_ranker_cached_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "rr_ranker_cached_fwd": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                                            ctypes.c_size_t, _P]),
     "rr_cand_only_plan": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P,
                                          ctypes.c_size_t, _P]),
     "rr_cand_only_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
@@ -445,3 +453,112 @@ def rr_rope_qk(q, k, offsets, cand_start, pos_base=None, theta_base=None, q_out=
                                          _ptr(cand_start), _ptr(pos_base), B, T, H, d, dt,
                                          float(theta_base or 0.0), _stream(stream, dev)))
     return outs[0], outs[1]
+
+
+class RRLayer(ctypes.Structure):
+    """rr_layer: device pointers of one layer's norm gain, W_qkv and W_o."""
+    _fields_ = [("norm_gain", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p)]
+
+
+def rr_rms_norm(x, gain, eps=None, out=None, stream=None) -> torch.Tensor:
+    """bf16 rows x / sqrt(mean(x^2) + eps) * gain; x float32 [M, D]."""
+    _need(x, "x", torch.float32)
+    _need(gain, "gain", torch.float32, x.device)
+    M, D = x.shape
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, x.device)
+    _check("rr_rms_norm", _lib.rr_rms_norm(_ptr(x), _ptr(gain), _ptr(out), M, D, float(eps or 0.0),
+                                           _stream(stream, x.device)))
+    return out
+
+
+def rr_linear(a, w, out=None, residual=None, stream=None) -> torch.Tensor:
+    """a W^T for a bf16 [M, K] and W bf16 [N, K]: into a new or given bf16 ``out``, or added
+    to a float32 ``residual`` [M, N] (returned)."""
+    _need(a, "a", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, a.device)
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K]")
+    if residual is not None:
+        _need(residual, "residual", torch.float32, a.device)
+    elif out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if out is not None:
+        _need(out, "out", torch.bfloat16, a.device)
+    _check("rr_linear", _lib.rr_linear(_ptr(a), _ptr(w), _ptr(out), _ptr(residual), M, N, K,
+                                       _stream(stream, a.device)))
+    return residual if residual is not None else out
+
+
+def _layer_array(layers, D, dev):
+    arr = (RRLayer * len(layers))()
+    for i, (gain, w_qkv, w_o) in enumerate(layers):
+        _need(gain, "norm_gain", torch.float32, dev)
+        _need(w_qkv, "w_qkv", torch.bfloat16, dev)
+        _need(w_o, "w_o", torch.bfloat16, dev)
+        if gain.numel() != D or tuple(w_qkv.shape) != (3 * D, D) or tuple(w_o.shape) != (D, D):
+            raise ValueError(f"layer {i}: expected gain [D], w_qkv [3D, D], w_o [D, D] with D = {D}")
+        arr[i] = RRLayer(gain.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr())
+    return arr
+
+
+def rr_ranker_fwd(x, layers, n_cand_only, offsets, cand_start, Tc: int, H: int, d: int, theta_base=None,
+                  keep_cache=True, x_cand_out=None, x_hist_out=None, kv_cache=None, workspace=None,
+                  stream=None):
+    """The layer stack over x float32 [T, H*d] (updated in place by the full layers).
+    ``layers``: list of (norm_gain float32 [D], w_qkv bf16 [3D, D], w_o bf16 [D, D]).
+    Returns (x_cand [Tc, D], x_hist [T-Tc, D], kv_cache bf16 [L, 2, T-Tc, H, d] or None)."""
+    dev = x.device
+    _need(x, "x", torch.float32)
+    T, D = x.shape
+    if D != H * d:
+        raise ValueError("x must be [T, H*d]")
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    B = offsets.numel() - 1
+    arr = _layer_array(layers, D, dev)
+    Th = T - Tc
+    if x_cand_out is None:
+        x_cand_out = torch.empty((Tc, D), dtype=torch.float32, device=dev)
+    if x_hist_out is None:
+        x_hist_out = torch.empty((Th, D), dtype=torch.float32, device=dev)
+    if kv_cache is None and keep_cache:
+        kv_cache = torch.empty((len(layers), 2, Th, H, d), dtype=torch.bfloat16, device=dev)
+    for name, t in (("x_cand_out", x_cand_out), ("x_hist_out", x_hist_out)):
+        _need(t, name, torch.float32, dev)
+    if kv_cache is not None:
+        _need(kv_cache, "kv_cache", torch.bfloat16, dev)
+        if kv_cache.numel() != len(layers) * 2 * Th * D:
+            raise ValueError("kv_cache must be [n_layers, 2, T - Tc, H, d]")
+    ws = _workspace(int(_lib.rr_ranker_workspace_bytes(B, T, Tc, H, d)), workspace, dev)
+    _check("rr_ranker_fwd", _lib.rr_ranker_fwd(
+        _ptr(x), ctypes.cast(arr, ctypes.c_void_p), len(layers), int(n_cand_only), _ptr(offsets),
+        _ptr(cand_start), B, T, Tc, H, d, float(theta_base or 0.0), _ptr(x_cand_out), _ptr(x_hist_out),
+        _ptr(kv_cache), _ptr(ws), ws.numel(), _stream(stream, dev)))
+    return x_cand_out, x_hist_out, kv_cache
+
+
+def rr_ranker_cached_fwd(x_cand, layers, kv_cache, hist_offsets, cand_offsets, H: int, d: int,
+                         theta_base=None, workspace=None, stream=None) -> torch.Tensor:
+    """A later request: candidates float32 [Tc, H*d] through every layer as a candidate-only
+    layer over ``kv_cache`` (from rr_ranker_fwd); updated in place and returned."""
+    dev = x_cand.device
+    _need(x_cand, "x_cand", torch.float32)
+    Tc, D = x_cand.shape
+    _need(kv_cache, "kv_cache", torch.bfloat16, dev)
+    _need(hist_offsets, "hist_offsets", torch.int32, dev)
+    _need(cand_offsets, "cand_offsets", torch.int32, dev)
+    B = cand_offsets.numel() - 1
+    Th = kv_cache.shape[2]
+    if kv_cache.shape[0] != len(layers) or kv_cache.numel() != len(layers) * 2 * Th * D:
+        raise ValueError("kv_cache must be [n_layers, 2, Th, H, d]")
+    arr = _layer_array(layers, D, dev)
+    ws = _workspace(int(_lib.rr_ranker_cached_workspace_bytes(B, Th, Tc, H, d)), workspace, dev)
+    _check("rr_ranker_cached_fwd", _lib.rr_ranker_cached_fwd(
+        _ptr(x_cand), ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(kv_cache), _ptr(hist_offsets),
+        _ptr(cand_offsets), B, Th, Tc, H, d, float(theta_base or 0.0), _ptr(ws), ws.numel(),
+        _stream(stream, dev)))
+    return x_cand

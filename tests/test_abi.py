@@ -170,6 +170,42 @@ def test_backward_argument_errors():
                                None) == rr.RR_EINVAL
 
 
+def test_ranker_argument_errors():
+    rr, lib = _lib()
+    layer = rr.RRLayer(0x1000, 0x1000, 0x1000)
+    arr = (rr.RRLayer * 2)(layer, layer)
+    null_layer = (rr.RRLayer * 2)(layer, rr.RRLayer(0x1000, None, 0x1000))
+
+    def call(**kw):
+        a = dict(x=FAKE, layers=arr, n=2, nco=1, off=FAKE, cs=FAKE, B=2, T=100, Tc=10, H=4, d=64, xc=FAKE,
+                 ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.rr_ranker_fwd(a["x"], ctypes.cast(a["layers"], ctypes.c_void_p) if a["layers"] else None,
+                                 a["n"], a["nco"], a["off"], a["cs"], a["B"], a["T"], a["Tc"], a["H"], a["d"], 0.0,
+                                 a["xc"], None, None, a["ws"], a["ws_bytes"], None)
+    assert call(d=16) == rr.RR_EUNSUPPORTED                 # the MFMA attention: d 32, 64, 128
+    assert call(H=3) == rr.RR_EUNSUPPORTED                  # D = 192 is not a multiple of 128
+    assert call(Tc=101) == rr.RR_EINVAL
+    assert call(nco=3) == rr.RR_EINVAL
+    assert call(layers=null_layer) == rr.RR_EINVAL
+    assert call(layers=None) == rr.RR_EINVAL
+    assert call(x=None) == rr.RR_EINVAL
+    assert call(xc=None) == rr.RR_EINVAL
+    assert call(ws=None) == rr.RR_EWORKSPACE
+    need = lib.rr_ranker_workspace_bytes(2, 100, 10, 4, 64)
+    assert need > lib.rr_attn_workspace_bytes(2, 100, 4, 64)
+    assert call(ws_bytes=need - 1) == rr.RR_EWORKSPACE
+    assert call(B=0, x=None, ws=None) == rr.RR_OK
+    assert lib.rr_ranker_workspace_bytes(2, 100, 10, 4, 16) == 0
+    assert lib.rr_ranker_cached_workspace_bytes(2, 90, 10, 4, 64) > 0
+    assert lib.rr_ranker_cached_fwd(None, ctypes.cast(arr, ctypes.c_void_p), 2, FAKE, FAKE, FAKE, 2, 90, 10, 4, 64,
+                                    0.0, FAKE, 1 << 40, None) == rr.RR_EINVAL
+    assert lib.rr_linear(FAKE, FAKE, FAKE, None, 10, 100, 64, None) == rr.RR_EUNSUPPORTED   # N % 128
+    assert lib.rr_linear(FAKE, FAKE, FAKE, None, 10, 128, 48, None) == rr.RR_EUNSUPPORTED   # K % 64
+    assert lib.rr_linear(FAKE, FAKE, FAKE, FAKE, 10, 128, 64, None) == rr.RR_EINVAL          # both outputs
+    assert lib.rr_rms_norm(FAKE, FAKE, FAKE, 3, 6, 0.0, None) == rr.RR_EINVAL                # D % 4
+
+
 def test_workspace_size_grows_with_work():
     _, lib = _lib()
     a = lib.rr_attn_workspace_bytes(64, 16000, 4, 64)

@@ -1,0 +1,205 @@
+"""GPU tests of the layer stack (rr_linear, rr_rms_norm, rr_ranker_fwd, rr_ranker_cached_fwd)
+against the oracle (oracle/ranker.py) and the page's invariants."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _gpu import gpu, needs_gpu, rr, to_dev
+from oracle import ranker as RK
+
+pytestmark = [gpu, needs_gpu]
+U = 2.0 ** -8          # bf16 unit roundoff (8 significant bits)
+F32 = 2.0 ** -24
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _layout(prefix, hist, cand):
+    L = np.asarray(prefix) + np.asarray(hist) + np.asarray(cand)
+    off = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    cs = (off[:-1] + np.asarray(prefix) + np.asarray(hist)).astype(np.int32)
+    return off, cs
+
+
+# users: a long history, no history at all (candidates read only themselves), no
+# candidates, a single candidate, a prefix-only history
+SHAPES = dict(prefix=[4, 0, 0, 3, 1, 2], hist=[300, 0, 45, 700, 129, 0], cand=[37, 6, 0, 128, 1, 5])
+
+
+def _setup(H, d, n_layers, seed, shapes=SHAPES):
+    off, cs = _layout(**shapes)
+    T = int(off[-1])
+    x, layers = W.ranker_inputs(seed, T, n_layers, H * d)
+    dev_layers = [(to_dev(g), to_dev(wq, torch.bfloat16), to_dev(wo, torch.bfloat16)) for g, wq, wo in layers]
+    or_layers = [RK.Layer(g.astype(np.float64), wq.astype(np.float64), wo.astype(np.float64))
+                 for g, wq, wo in layers]
+    return x, off, cs, dev_layers, or_layers
+
+
+def _run(x, off, cs, dev_layers, n_cand_only, H, d):
+    Tc = int((off[1:] - cs).sum())
+    xd = to_dev(x.copy())
+    xc, xh, cache = rr().rr_ranker_fwd(xd, dev_layers, n_cand_only, to_dev(off), to_dev(cs), Tc, H, d)
+    torch.cuda.synchronize()
+    return xd, xc, xh, cache
+
+
+def test_linear_bounds_and_rows():
+    rng = np.random.default_rng(1)
+    for M, N, K in ((1, 128, 64), (129, 384, 256), (300, 256, 512)):
+        a = W.round_to_bf16(rng.standard_normal((M, K)).astype(np.float32)).astype(np.float64)
+        w = W.round_to_bf16((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)).astype(np.float64)
+        ad, wd = to_dev(a, torch.bfloat16), to_dev(w, torch.bfloat16)
+        got = _np(rr().rr_linear(ad, wd))
+        ref = a @ w.T
+        mag = np.abs(a) @ np.abs(w).T
+        # exact bf16 products summed in fp32 (at most K roundings), then one rounding to bf16
+        assert np.all(np.abs(got - ref) <= U * np.abs(ref) + (K + 2) * F32 * mag), (M, N, K)
+        res0 = rng.standard_normal((M, N)).astype(np.float32)
+        res = to_dev(res0.copy())
+        rr().rr_linear(ad, wd, residual=res)
+        got_r = _np(res)
+        assert np.all(np.abs(got_r - (res0 + ref)) <= (K + 2) * F32 * (mag + np.abs(res0))), (M, N, K)
+        # a row's result does not depend on the other rows of the launch
+        r = M // 2
+        one = rr().rr_linear(ad[r:r + 1].contiguous(), wd)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(one)[0], got[r])
+
+
+def test_rms_norm_bounds():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((37, 256)) * rng.uniform(0.01, 20, (37, 1))).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(256)).astype(np.float32)
+    got = _np(rr().rr_rms_norm(to_dev(x), to_dev(g)))
+    ref = RK.rms_norm(x, g)
+    # float32 evaluation (relative 2^-20 covers its few roundings), one rounding to bf16
+    assert np.all(np.abs(got - ref) <= (U + 2.0 ** -20) * np.abs(ref) + 1e-30)
+
+
+def _frob(got, ref, base, what):
+    """Relative Frobenius error of a layer's update (got - base against ref - base)."""
+    e = np.linalg.norm(got - ref) / max(np.linalg.norm(ref - base), 1e-30)
+    # about five bf16 roundings on the update's path (norm, projections, rotation, attention
+    # weights and output), independent errors of relative size u / sqrt(3) each: ~1.3 u;
+    # bound 4 u
+    assert e <= 4 * U, f"{what}: relative error {e:.4f} > {4 * U:.4f}"
+
+
+@pytest.mark.parametrize("H,d", [(4, 64), (4, 128)])
+def test_each_layer_against_oracle(H, d):
+    """The stack run with its first l layers, l = 1..L: layer l's update against the oracle's
+    layer applied to the GPU's state before it (no error carried between layers)."""
+    n_layers, n_cand_only = 4, 2
+    x, off, cs, dl, ol = _setup(H, d, n_layers, seed=40 + d)
+    xh0, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    prev_full, prev_c, prev_h = x.astype(np.float64), None, None
+    n_full = n_layers - n_cand_only
+    for l in range(1, n_layers + 1):
+        nco = max(0, l - n_full)
+        xd, xc, xh, _ = _run(x, off, cs, dl[:l], nco, H, d)
+        if l <= n_full:
+            got = _np(xd)
+            ref = RK.block_full(prev_full, ol[l - 1], off, cs, H, d)
+            _frob(got, ref, prev_full, f"full layer {l}")
+            prev_full = got
+            prev_h, prev_c = RK.split_history_and_candidates(got, off, cs)[:2]
+            assert np.array_equal(_np(xc), prev_c) and np.array_equal(_np(xh), prev_h)
+        else:
+            assert np.array_equal(_np(xh), prev_h), "the history moved in a candidate-only layer"
+            kh, vh = RK.history_kv(prev_h, ol[l - 1], hoff, H, d)
+            ref = RK.block_cand_only(prev_c, kh, vh, ol[l - 1], hoff, coff, H, d)
+            got = _np(xc)
+            _frob(got, ref, prev_c, f"candidate-only layer {l}")
+            prev_c = got
+
+
+def test_stack_is_the_composition_of_its_parts():
+    """rr_ranker_fwd equals, bit for bit, the same layers written out with the separately
+    tested entry points (rr_rms_norm, rr_linear, rr_rope_qk, rr_attn_fwd,
+    rr_cand_only_attn_fwd) and plain row gathers for the split and the cache."""
+    H, d, n_layers, nco = 4, 64, 3, 1
+    x, off, cs, dl, _ = _setup(H, d, n_layers, seed=50)
+    xd, xc, xh, cache = _run(x, off, cs, dl, nco, H, d)
+    R = rr()
+    D = H * d
+    offd, csd = to_dev(off), to_dev(cs)
+    hist_rows = np.concatenate([np.arange(off[b], cs[b]) for b in range(len(cs))]).astype(np.int64)
+    cand_rows = np.concatenate([np.arange(cs[b], off[b + 1]) for b in range(len(cs))]).astype(np.int64)
+    hi, ci = to_dev(hist_rows), to_dev(cand_rows)
+    hoff = to_dev(np.concatenate([[0], np.cumsum(cs - off[:-1])]).astype(np.int32))
+    coff = to_dev(np.concatenate([[0], np.cumsum(off[1:] - cs)]).astype(np.int32))
+    hlen = to_dev((cs - off[:-1]).astype(np.int32))
+    s = to_dev(x.copy())
+    T = s.shape[0]
+    for l, (g, wq, wo) in enumerate(dl[:n_layers - nco]):
+        qkv = R.rr_linear(R.rr_rms_norm(s, g), wq)
+        q, k, v = (qkv[:, i * D:(i + 1) * D].contiguous().view(T, H, d) for i in range(3))
+        q, k = R.rr_rope_qk(q, k, offd, csd)
+        assert torch.equal(cache[l, 0], k[hi]) and torch.equal(cache[l, 1], v[hi]), l
+        o = R.rr_attn_fwd(q, k, v, offd, csd)
+        R.rr_linear(o.view(T, D), wo, residual=s)
+    torch.cuda.synchronize()
+    assert torch.equal(s, xd)
+    sh, sc = s[hi].contiguous(), s[ci].contiguous()
+    for l in range(n_layers - nco, n_layers):
+        g, wq, wo = dl[l]
+        kv = R.rr_linear(R.rr_rms_norm(sh, g), wq[D:].contiguous())
+        kh, vh = (kv[:, i * D:(i + 1) * D].contiguous().view(-1, H, d) for i in range(2))
+        _, kh = R.rr_rope_qk(None, kh, hoff, hoff[1:].contiguous())
+        assert torch.equal(cache[l, 0], kh) and torch.equal(cache[l, 1], vh), l
+        qkv = R.rr_linear(R.rr_rms_norm(sc, g), wq)
+        Tc = sc.shape[0]
+        q, k, v = (qkv[:, i * D:(i + 1) * D].contiguous().view(Tc, H, d) for i in range(3))
+        q, k = R.rr_rope_qk(q, k, coff, coff[:-1].contiguous(), pos_base=hlen)
+        o = R.rr_cand_only_attn_fwd(q, kh, vh, k, v, hoff, coff)
+        R.rr_linear(o.view(Tc, D), wo, residual=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, xc) and torch.equal(sh, xh)
+
+
+def test_cached_request_bit_identical():
+    """A later request with the same users: the cached pass reproduces the full pass's
+    candidates bit for bit, also for a new set of candidates."""
+    H, d, n_layers, nco = 4, 128, 4, 2
+    x, off, cs, dl, _ = _setup(H, d, n_layers, seed=60)
+    _, xc, xh, cache = _run(x, off, cs, dl, nco, H, d)
+    xh0, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    again = rr().rr_ranker_cached_fwd(to_dev(xc0.astype(np.float32)), dl, cache, to_dev(hoff.astype(np.int32)),
+                                      to_dev(coff.astype(np.int32)), H, d)
+    torch.cuda.synchronize()
+    assert torch.equal(again, xc)
+    # new candidates for the same users (other counts): the full pass on the new layout
+    rng = np.random.default_rng(61)
+    newc = np.array([3, 0, 9, 1, 4, 2])
+    prefix, hist = np.array(SHAPES["prefix"]), np.array(SHAPES["hist"])
+    off2, cs2 = _layout(prefix, hist, newc)
+    x2 = np.concatenate([np.concatenate([x[off[b]:cs[b]], rng.standard_normal((newc[b], x.shape[1]))])
+                         for b in range(len(newc))]).astype(np.float32)
+    _, xc2, xh2, cache2 = _run(x2, off2, cs2, dl, nco, H, d)
+    assert torch.equal(xh2, xh) and torch.equal(cache2, cache)
+    c2 = RK.split_history_and_candidates(x2, off2, cs2)
+    cached = rr().rr_ranker_cached_fwd(to_dev(c2[1].astype(np.float32)), dl, cache,
+                                       to_dev(hoff.astype(np.int32)), to_dev(c2[3].astype(np.int32)), H, d)
+    torch.cuda.synchronize()
+    assert torch.equal(cached, xc2)
+
+
+def test_candidate_order_bit_identical():
+    H, d, n_layers, nco = 4, 64, 3, 1
+    x, off, cs, dl, _ = _setup(H, d, n_layers, seed=70)
+    _, xc, xh, _ = _run(x, off, cs, dl, nco, H, d)
+    b = 3
+    perm = np.arange(len(x))
+    perm[cs[b]:off[b + 1]] = cs[b] + np.random.default_rng(7).permutation(off[b + 1] - cs[b])
+    _, xc2, xh2, _ = _run(x[perm], off, cs, dl, nco, H, d)
+    coff = np.concatenate([[0], np.cumsum(off[1:] - cs)])
+    cperm = np.arange(int(coff[-1]))
+    cperm[coff[b]:coff[b + 1]] = coff[b] + (perm[cs[b]:off[b + 1]] - cs[b])
+    assert torch.equal(xh2, xh)
+    assert torch.equal(xc2, xc[to_dev(cperm)])

@@ -233,6 +233,21 @@ def draw_output_grad(seed: int, T: int, H: int, d: int, dtype: str = "bf16",
     return _draw(int(seed), 3, T, H, d, scaled, dtype)
 
 
+def ranker_inputs(seed: int, T: int, n_layers: int, D: int):
+    """Inputs of a layer stack: states x ~ N(0, 1) float32 [T, D], and per layer a norm gain
+    1 + 0.1 N(0, 1) (float32 [D]) and projections W_qkv [3D, D], W_o [D, D] ~ N(0, 1/D) rounded
+    to bf16 (held as float32).  Streams 10.. of ``seed``."""
+    x = _draw(int(seed), 10, T, 1, D, False, "f32").reshape(T, D)
+    layers = []
+    for l in range(n_layers):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 11, l])))
+        gain = (1.0 + 0.1 * g.standard_normal(D)).astype(np.float32)
+        w_qkv = round_to_bf16((g.standard_normal((3 * D, D)) / math.sqrt(D)).astype(np.float32))
+        w_o = round_to_bf16((g.standard_normal((D, D)) / math.sqrt(D)).astype(np.float32))
+        layers.append((gain, w_qkv, w_o))
+    return x, layers
+
+
 def split_to_cand_only(fb: FullBatch) -> CandOnlyBatch:
     """Re-express a full batch without padding as candidate-only inputs.
 
