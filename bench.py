@@ -12,6 +12,12 @@ inputs (>= 1 GiB in total) that no step finds its data in the 256 MB Infinity Ca
 metric: effective (non-pad) attention TFLOP/s = 4 * d * H * sum_b [n_b^2 + c_b (n_b + 1)]
 per step / step time; candidates/s is reported beside it.
 
+``--ranker`` (full-sequence bf16 workloads) runs the ranker's layer stack instead: 6 full
+layers, the split, 2 candidate-only layers (``rr_ranker_fwd``), with random bf16
+projections of width D = H d; the line reports candidates/s of a whole request, and of
+a later request for the same users that reuses the history's keys and values
+(``rr_ranker_cached_fwd``).
+
 ``--backward`` (full-sequence bf16 workloads) makes a step one training pass of the
 attention: plan, forward with the log-sum-exp (``rr_attn_run_lse``) and the backward
 (``rr_attn_bwd_run``: dq, dk, dv).  The backward counts 2.5x the forward's effective
@@ -49,6 +55,8 @@ def parse_args():
                         "before the attention")
     p.add_argument("--backward", action="store_true",
                    help="a step is plan + forward with lse + backward (full-sequence bf16, d 64 or 128)")
+    p.add_argument("--ranker", action="store_true",
+                   help="the layer stack (6 full + 2 candidate-only layers) end to end; candidates/s")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -295,6 +303,141 @@ def cpu_baseline(cfg, b, budget_s, rope=False, backward=False):
             "sample": sample, "seconds": round(dt, 2), "candidates_per_s": done_cands / dt}
 
 
+RANKER_LAYERS, RANKER_CAND_ONLY = 8, 2
+
+
+def ranker_counts(b):
+    """(GEMM FLOPs, attention FLOPs) of one full request of the layer stack."""
+    import numpy as np
+    from jagged_candidate_isolated_amd import accounting as acc
+    D = b.H * b.d
+    Tc = int(b.cand.sum())
+    Th = b.T - Tc
+    n_full = RANKER_LAYERS - RANKER_CAND_ONLY
+    gemm = n_full * 8.0 * b.T * D * D + RANKER_CAND_ONLY * (4.0 * Th * D * D + 8.0 * Tc * D * D)
+    eff, _ = acc.full_mode_counts(b.prefix, b.hist, b.cand, b.pad, b.attend_padded_history)
+    hl = b.prefix + b.hist
+    pairs = acc.cand_only_pairs(hl, b.cand)
+    attn = n_full * acc.attention_flops(eff, b.H, b.d) + RANKER_CAND_ONLY * acc.attention_flops(pairs, b.H, b.d)
+    return gemm, attn
+
+
+def ranker_cached_counts(b):
+    from jagged_candidate_isolated_amd import accounting as acc
+    D = b.H * b.d
+    Tc = int(b.cand.sum())
+    pairs = acc.cand_only_pairs(b.prefix + b.hist, b.cand)
+    return RANKER_LAYERS * 8.0 * Tc * D * D, RANKER_LAYERS * acc.attention_flops(pairs, b.H, b.d)
+
+
+def run_ranker(args, b, torch, rr):
+    """The layer stack end to end: a full request and a cached request, graph-replayed."""
+    import numpy as np
+    import workloads as W
+    dev = torch.device("cuda:0")
+    D = b.H * b.d
+    Tc = int(b.cand.sum())
+    Th = b.T - Tc
+    x0, layers = W.ranker_inputs(b.seed + 99, b.T, RANKER_LAYERS, D)
+    dl = [(torch.from_numpy(g).to(dev), torch.from_numpy(wq).to(dev).to(torch.bfloat16),
+           torch.from_numpy(wo).to(dev).to(torch.bfloat16)) for g, wq, wo in layers]
+    x_src = torch.from_numpy(x0).to(dev)
+    x = torch.empty_like(x_src)
+    off = torch.from_numpy(b.offsets).to(dev)
+    cst = torch.from_numpy(b.cand_start).to(dev)
+    xc = torch.empty((Tc, D), dtype=torch.float32, device=dev)
+    xh = torch.empty((Th, D), dtype=torch.float32, device=dev)
+    cache = torch.empty((RANKER_LAYERS, 2, Th, b.H, b.d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rr.rr_ranker_workspace_bytes(b.B, b.T, Tc, b.H, b.d), dtype=torch.uint8, device=dev)
+    hoff = torch.from_numpy(np.concatenate([[0], np.cumsum(b.cand_start - b.offsets[:-1])]).astype(np.int32)).to(dev)
+    coff = torch.from_numpy(np.concatenate([[0], np.cumsum(b.offsets[1:] - b.cand_start)]).astype(np.int32)).to(dev)
+    cand_rows = np.concatenate([np.arange(b.cand_start[u], b.offsets[u + 1]) for u in range(b.B)]).astype(np.int64)
+    xc_src = x_src[torch.from_numpy(cand_rows).to(dev)].contiguous()
+    xc2 = torch.empty_like(xc_src)
+    ws2 = torch.empty(rr.rr_ranker_cached_workspace_bytes(b.B, Th, Tc, b.H, b.d), dtype=torch.uint8, device=dev)
+
+    def full_step():
+        x.copy_(x_src)
+        rr.rr_ranker_fwd(x, dl, RANKER_CAND_ONLY, off, cst, Tc, b.H, b.d, x_cand_out=xc, x_hist_out=xh,
+                         kv_cache=cache, workspace=ws)
+
+    def cached_step():
+        xc2.copy_(xc_src)
+        rr.rr_ranker_cached_fwd(xc2, dl, cache, hoff, coff, b.H, b.d, workspace=ws2)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    full_step(); torch.cuda.synchronize()
+    t = time.perf_counter(); full_step(); torch.cuda.synchronize()
+    est = time.perf_counter() - t
+    steps = args.steps or int(min(2000, max(10, 1.0 / max(est, 1e-6))))
+    warmup = args.warmup if args.warmup is not None else max(3, steps // 10)
+    ms_full = timed(full_step, steps, warmup)
+    ms_cached = timed(cached_step, steps, warmup)
+    # the cached request reproduces the full request's candidates
+    full_step(); cached_step(); torch.cuda.synchronize()
+    same = bool(torch.equal(xc, xc2))
+    gemm_f, attn_f = ranker_counts(b)
+    gemm_c, attn_c = ranker_cached_counts(b)
+    out = {
+        "metric": "ranker layer stack (6 full + 2 candidate-only layers) end to end, candidates/s",
+        "value": Tc / (ms_full / 1e3), "unit": "candidates/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_full, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (random projections)",
+        "config": dict(describe(args.config, b), parallelism="none (1 GPU)", layers=RANKER_LAYERS,
+                       cand_only_layers=RANKER_CAND_ONLY, D=D,
+                       step="copy of the input states + rr_ranker_fwd (kv cache written)"),
+        "ranker": {
+            "full_request": {"ms": ms_full, "candidates_per_s": Tc / (ms_full / 1e3),
+                             "gemm_tflop": gemm_f / 1e12, "attention_tflop": attn_f / 1e12,
+                             "tflops": (gemm_f + attn_f) / (ms_full / 1e3) / 1e12},
+            "cached_request": {"ms": ms_cached, "candidates_per_s": Tc / (ms_cached / 1e3),
+                               "gemm_tflop": gemm_c / 1e12, "attention_tflop": attn_c / 1e12,
+                               "tflops": (gemm_c + attn_c) / (ms_cached / 1e3) / 1e12,
+                               "bit_identical_to_full": same},
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = ranker_cpu_baseline(b, x0, layers, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def ranker_cpu_baseline(b, x0, layers, budget_s):
+    """The oracle's layer stack on the first users of the batch, one user at a time, until
+    about ``budget_s`` of CPU time; candidates/s."""
+    import numpy as np
+    from oracle import ranker as RK
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    ol = [RK.Layer(g.astype(np.float64), wq.astype(np.float64), wo.astype(np.float64)) for g, wq, wo in layers]
+    t0 = time.perf_counter()
+    users = cands = 0
+    while time.perf_counter() - t0 < budget_s and users < b.B:
+        lo, cs, hi = int(b.offsets[users]), int(b.cand_start[users]), int(b.offsets[users + 1])
+        RK.ranker_forward(x0[lo:hi], ol, RANKER_CAND_ONLY, [0, hi - lo], [cs - lo], b.H, b.d)
+        cands += hi - cs
+        users += 1
+    dt = time.perf_counter() - t0
+    return {"value": cands / dt, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {users} of {b.B} users, float64 layer-stack oracle", "seconds": round(dt, 2)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -310,6 +453,13 @@ def main():
         return
     cfg = args.config
     b = make_batch(cfg)
+    if args.ranker:
+        if cfg in (4, 6, 7) or b.dtype != "bf16" or b.d not in (32, 64, 128) or (b.H * b.d) % 128:
+            print("--ranker runs the full-sequence bf16 workloads without padding (configs 2, 3, 5)",
+                  file=sys.stderr)
+            sys.exit(2)
+        run_ranker(args, b, torch, rr)
+        return
     if args.backward and (cfg == 4 or b.dtype != "bf16" or b.d not in (64, 128) or args.rope):
         print("--backward runs the full-sequence bf16 workloads with d 64 or 128 (configs 2, 3, 5, 6, 7), "
               "without --rope", file=sys.stderr)

@@ -562,3 +562,11 @@ def rr_ranker_cached_fwd(x_cand, layers, kv_cache, hist_offsets, cand_offsets, H
         _ptr(cand_offsets), B, Th, Tc, H, d, float(theta_base or 0.0), _ptr(ws), ws.numel(),
         _stream(stream, dev)))
     return x_cand
+
+
+def rr_ranker_workspace_bytes(B: int, T: int, Tc: int, H: int, d: int) -> int:
+    return int(_lib.rr_ranker_workspace_bytes(B, T, Tc, H, d))
+
+
+def rr_ranker_cached_workspace_bytes(B: int, Th: int, Tc: int, H: int, d: int) -> int:
+    return int(_lib.rr_ranker_cached_workspace_bytes(B, Th, Tc, H, d))
