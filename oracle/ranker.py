@@ -21,6 +21,16 @@ with W_qkv [3D, D], W_o [D, D] (out x in), D = H d, heads laid out [H, d] inside
 row, rms_norm(x) = x / sqrt(mean(x^2) + eps), eps = 1e-6.  A frozen history row of a
 candidate-only layer gives its key and value through that layer's own norm and
 projections (and its rotary position).  No feed-forward block and no action head.
+
+``candidate_only_layers_update_user_token`` (named on the page, section "只更新候选的末尾层",
+with no further definition; off by default there).  Reading taken: with it on, a user's
+prefix rows (the user tokens) keep being updated in the candidate-only layers, under the
+same attention contract as in the full layers (they read the prefix and history rows,
+never candidates); only the history rows stay frozen.  Such a layer is the page's
+fallback with the prefix rows kept: the full layer over [prefix (current) | history
+(frozen) | candidates (current)], after which the history rows are put back to their
+frozen states.  The prefix never reads a candidate, so the keys and values a later
+request reuses stay candidate-independent.
 """
 from __future__ import annotations
 
@@ -101,11 +111,47 @@ def split_history_and_candidates(x, offsets, cand_start):
     return x[hidx], x[cidx], hoff, coff
 
 
-def ranker_forward(x, layers, n_cand_only, offsets, cand_start, H, d, base=DEFAULT_BASE, scale=None):
+def _user_token_layer(x_p, x_h, x_c, layer, p, hist_offsets, cand_offsets, H, d, base, scale):
+    """One candidate-only layer that also updates the user tokens: the full layer over each
+    user's [prefix x_p | frozen history x_h | candidates x_c], history rows put back.
+    p[b] = user b's prefix rows, the first p[b] rows of its block in hist_offsets (those of
+    x_h are the frozen copies, replaced here by x_p).  Returns (x_p, x_c, k_ph, v_ph): the
+    new prefix and candidate states and the keys (rotated) and values of [prefix | history]
+    rows this layer read."""
+    hoff = np.asarray(hist_offsets, np.int64)
+    coff = np.asarray(cand_offsets, np.int64)
+    poff = np.concatenate([[0], np.cumsum(p)]).astype(np.int64)
+    rows, offs, cs = [], [0], []
+    for b in range(len(p)):
+        blk = np.concatenate([x_p[poff[b]:poff[b + 1]], x_h[hoff[b] + p[b]:hoff[b + 1]], x_c[coff[b]:coff[b + 1]]])
+        rows.append(blk)
+        cs.append(offs[-1] + hoff[b + 1] - hoff[b])
+        offs.append(offs[-1] + len(blk))
+    X = np.concatenate(rows) if rows else np.zeros((0, x_c.shape[1]))
+    offs, cs = np.asarray(offs, np.int64), np.asarray(cs, np.int64)
+    _, k, v = _qkv(X, layer, H, d)
+    kr = rope(k, right_anchored_positions(offs, cs), base)
+    Y = block_full(X, layer, offs, cs, H, d, base, scale)
+    new_p, new_c, k_ph, v_ph = [], [], [], []
+    for b in range(len(p)):
+        lo, c = offs[b], cs[b]
+        new_p.append(Y[lo:lo + p[b]])
+        new_c.append(Y[c:offs[b + 1]])
+        k_ph.append(kr[lo:c]); v_ph.append(v[lo:c])
+    cat = lambda parts, w: np.concatenate(parts) if parts else np.zeros((0,) + w)
+    return (cat(new_p, (x_c.shape[1],)), cat(new_c, (x_c.shape[1],)), cat(k_ph, (H, d)), cat(v_ph, (H, d)))
+
+
+def ranker_forward(x, layers, n_cand_only, offsets, cand_start, H, d, base=DEFAULT_BASE, scale=None,
+                   user_tokens=None):
     """The layer stack over x [T, D]: len(layers) - n_cand_only full layers, the split, then
-    n_cand_only candidate-only layers.  Returns (x_cand [Tc, D], x_hist [Th, D] (frozen),
-    cache): cache[l] = (k_hist, v_hist) of layer l for the history rows, the keys and values
-    a later request reuses."""
+    n_cand_only candidate-only layers.  Returns (x_cand [Tc, D], x_hist [Th, D], cache):
+    x_hist = the states of each user's rows before its candidate start after the last layer
+    (frozen, or with ``user_tokens`` the prefix rows updated); cache[l] = (k_hist, v_hist)
+    of layer l for those rows, the keys and values a later request reuses.
+
+    ``user_tokens`` (int [B], prefix rows per user, or None): candidate_only_layers_update_user_token
+    on, under the reading in this module's header."""
     n_full = len(layers) - n_cand_only
     cache = []
     for layer in layers[:n_full]:
@@ -116,10 +162,21 @@ def ranker_forward(x, layers, n_cand_only, offsets, cand_start, H, d, base=DEFAU
         cache.append((kh.reshape(-1, H, d), vh.reshape(-1, H, d)))
         x = block_full(x, layer, offsets, cand_start, H, d, base, scale)
     x_hist, x_cand, hoff, coff = split_history_and_candidates(x, offsets, cand_start)
+    if user_tokens is None:
+        for layer in layers[n_full:]:
+            kh, vh = history_kv(x_hist, layer, hoff, H, d, base)
+            cache.append((kh, vh))
+            x_cand = block_cand_only(x_cand, kh, vh, layer, hoff, coff, H, d, base, scale)
+        return x_cand, x_hist, cache
+    p = np.asarray(user_tokens, np.int64)
+    x_p = np.concatenate([x_hist[hoff[b]:hoff[b] + p[b]] for b in range(len(p))] + [np.zeros((0, x.shape[1]))])
     for layer in layers[n_full:]:
-        kh, vh = history_kv(x_hist, layer, hoff, H, d, base)
+        x_p, x_cand, kh, vh = _user_token_layer(x_p, x_hist, x_cand, layer, p, hoff, coff, H, d, base, scale)
         cache.append((kh, vh))
-        x_cand = block_cand_only(x_cand, kh, vh, layer, hoff, coff, H, d, base, scale)
+    poff = np.concatenate([[0], np.cumsum(p)])
+    x_hist = x_hist.copy()
+    for b in range(len(p)):
+        x_hist[hoff[b]:hoff[b] + p[b]] = x_p[poff[b]:poff[b + 1]]
     return x_cand, x_hist, cache
 
 

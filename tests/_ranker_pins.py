@@ -12,7 +12,9 @@ Each ``pin_*`` raises AssertionError when the oracle disagrees with
  * closed forms (W_o = 0 leaves every state unchanged; W_q = W_k = 0 with W_v = W_o = I
    gives each row the mean of its admitted normalised rows), or
  * the page's invariants: candidate order, history independence, and the cached request
-   (every layer candidate-only over the history keys and values) equal to the full one.
+   (every layer candidate-only over the history keys and values) equal to the full one,
+   also with the user tokens updated in the candidate-only layers (the same torch stack
+   with only the history rows frozen).
 They call the oracle through its module at call time, so tests can plant mistakes.
 """
 from __future__ import annotations
@@ -42,19 +44,22 @@ def make_stack(seed, n_layers=3, H=2, d=4, shapes=SHAPES):
     return x, layers, offsets, cand_start, H, d
 
 
-def _torch_stack(x, layers, n_cand_only, offsets, cand_start, H, d, base):
+def _torch_stack(x, layers, n_cand_only, offsets, cand_start, H, d, base, user_tokens=None):
     import torch
     import torch.nn.functional as F
     T, D = x.shape
     X = torch.from_numpy(np.asarray(x, np.float64))
     pos = torch.zeros(T, dtype=torch.float64)
     is_hist = torch.zeros(T, dtype=torch.bool)
+    frozen_rows = torch.zeros(T, dtype=torch.bool)
     users = []
     for b in range(len(cand_start)):
         lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        p = 0 if user_tokens is None else int(user_tokens[b])
         for r in range(lo, hi):
             pos[r] = min(r, cs) - lo          # newest history row at cs-1-lo, candidates at cs-lo
             is_hist[r] = r < cs
+            frozen_rows[r] = lo + p <= r < cs   # with user tokens updated, the prefix is not frozen
         # a row reads the rows before the candidate start, and a candidate also itself
         m = torch.tensor([[j < cs - lo or i == j for j in range(hi - lo)] for i in range(hi - lo)],
                          dtype=torch.bool).reshape(hi - lo, hi - lo)
@@ -83,8 +88,8 @@ def _torch_stack(x, layers, n_cand_only, offsets, cand_start, H, d, base):
         X = layer(X, L)
     frozen = X.clone()
     for L in layers[n_full:]:
-        X = torch.where(is_hist[:, None], frozen, layer(X, L))
-    return X[~is_hist].numpy(), frozen[is_hist].numpy()
+        X = torch.where(frozen_rows[:, None], frozen, layer(X, L))
+    return X[~is_hist].numpy(), X[is_hist].numpy()
 
 
 def pin_rms_norm():
@@ -107,6 +112,33 @@ def pin_torch_stack():
         want_c, want_h = _torch_stack(x, layers, n_cand_only, off, cs, H, d, base=50.0)
         assert np.max(np.abs(got_c - want_c)) <= 1e-10, seed
         assert np.max(np.abs(got_h - want_h)) <= 1e-10, seed
+
+
+def pin_user_tokens():
+    """candidate_only_layers_update_user_token: the torch stack with the prefix rows left
+    out of the frozen set; no user tokens is the default stack; the cached request and the
+    history's independence of candidates still hold."""
+    x, layers, off, cs, H, d = make_stack(41)
+    p = np.array(SHAPES["prefix"])
+    for n_cand_only in (1, 2):
+        got_c, got_h, _ = RK.ranker_forward(x, layers, n_cand_only, off, cs, H, d, base=50.0, user_tokens=p)
+        want_c, want_h = _torch_stack(x, layers, n_cand_only, off, cs, H, d, base=50.0, user_tokens=p)
+        assert np.max(np.abs(got_c - want_c)) <= 1e-10
+        assert np.max(np.abs(got_h - want_h)) <= 1e-10
+    base_c, base_h, base_cache = RK.ranker_forward(x, layers, 2, off, cs, H, d)
+    z_c, z_h, z_cache = RK.ranker_forward(x, layers, 2, off, cs, H, d, user_tokens=np.zeros_like(p))
+    assert np.max(np.abs(z_c - base_c)) <= 1e-12 and np.max(np.abs(z_h - base_h)) <= 1e-12
+    xc, xh, cache = RK.ranker_forward(x, layers, 2, off, cs, H, d, user_tokens=p)
+    assert np.max(np.abs(xh - base_h)) > 1e-3          # the prefix rows did move
+    _, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    again = RK.ranker_forward_cached(xc0, cache, layers, hoff, coff, H, d)
+    assert np.max(np.abs(again - xc)) <= 1e-12
+    x3 = x.copy()
+    x3[int(cs[0])] += 5.0
+    _, xh3, cache3 = RK.ranker_forward(x3, layers, 2, off, cs, H, d, user_tokens=p)
+    assert np.array_equal(xh3, xh)
+    for (k1, v1), (k2, v2) in zip(cache, cache3):
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
 
 
 def pin_closed_forms():
@@ -158,4 +190,4 @@ def pin_invariants():
     assert np.array_equal(xc3[1:], xc[1:])
 
 
-RANKER_PINS = [pin_rms_norm, pin_torch_stack, pin_closed_forms, pin_invariants]
+RANKER_PINS = [pin_rms_norm, pin_torch_stack, pin_user_tokens, pin_closed_forms, pin_invariants]
