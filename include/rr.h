@@ -292,8 +292,8 @@ int rr_rms_norm(const float* x, const float* gain, void* out, int32_t M, int32_t
 int rr_linear(const void* a, const void* w, void* out, float* residual, int32_t M, int32_t N, int32_t K,
               hipStream_t stream);
 
-/* Bytes of workspace rr_ranker_fwd needs (0 on unsupported sizes). */
-size_t rr_ranker_workspace_bytes(int32_t B, int32_t T, int32_t Tc, int32_t H, int32_t d);
+/* Bytes of workspace rr_ranker_fwd needs (0 on unsupported sizes); Tp = 0 without user tokens. */
+size_t rr_ranker_workspace_bytes(int32_t B, int32_t T, int32_t Tc, int32_t Tp, int32_t H, int32_t d);
 
 /*
  * rr_ranker_fwd -- one request: the whole stack over a jagged batch (no padding mask).
@@ -304,17 +304,42 @@ size_t rr_ranker_workspace_bytes(int32_t B, int32_t T, int32_t Tc, int32_t H, in
  * n_cand_only the last n_cand_only layers are candidate-only (0 <= n_cand_only <= n_layers)
  * offsets, cand_start  as rr_attn_fwd; Tc = total candidate rows (sum of offsets[b+1] -
  *             cand_start[b]), the caller's count; Th = T - Tc history rows
+ * user_tokens int32 [B] device or NULL: candidate_only_layers_update_user_token (section
+ *             "只更新候选的末尾层" names it, off by default, without defining it).  Reading:
+ *             with it, the first user_tokens[b] rows of user b (its user tokens, clamped to
+ *             its rows before cand_start) keep being updated in the candidate-only layers
+ *             under their full-layer contract (they read the user's rows before cand_start,
+ *             never candidates); only the other rows freeze.  Tp = sum of user_tokens (the
+ *             caller's count); ignored when user_tokens is NULL
  * x_cand_out  float [Tc][D] device, written: the candidates' final states, users in order
- * x_hist_out  float [Th][D] device or NULL: the frozen history states (rows before each
- *             user's candidate start, users in order)
+ * x_hist_out  float [Th][D] device or NULL: the states of the rows before each user's
+ *             candidate start, users in order (frozen; with user tokens, theirs updated)
  * kv_cache    bf16 [n_layers][2][Th][H][d] device or NULL: written with every layer's
  *             history keys (rotated) and values, for rr_ranker_cached_fwd
- * workspace   rr_ranker_workspace_bytes(B, T, Tc, H, d) bytes
+ * workspace   rr_ranker_workspace_bytes(B, T, Tc, Tp, H, d) bytes
  */
 int rr_ranker_fwd(float* x, const rr_layer* layers, int32_t n_layers, int32_t n_cand_only,
-                  const int32_t* offsets, const int32_t* cand_start, int32_t B, int32_t T, int32_t Tc,
-                  int32_t H, int32_t d, float theta_base, float* x_cand_out, float* x_hist_out,
-                  void* kv_cache, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                  const int32_t* offsets, const int32_t* cand_start, const int32_t* user_tokens, int32_t B,
+                  int32_t T, int32_t Tc, int32_t Tp, int32_t H, int32_t d, float theta_base, float* x_cand_out,
+                  float* x_hist_out, void* kv_cache, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * rr_user_token_attn_plan / _run -- jagged attention with no self-term: every query row of
+ * user b (rows query_offsets[b] .. query_offsets[b+1]) reads exactly the key rows of user b
+ * (key_offsets[b] .. key_offsets[b+1]); a query whose user has no keys gets 0.  These are the
+ * user tokens of candidate-only layers with candidate_only_layers_update_user_token (they
+ * read the user's prefix and frozen history, as in the full layers, and no candidate).
+ * q, o [Tq][H][d]; k, v [Tk][H][d]; dtype, scale and workspace as rr_cand_only_plan / _run
+ * (workspace: rr_user_token_attn_workspace_bytes).
+ */
+size_t rr_user_token_attn_workspace_bytes(int32_t B, int32_t Tk, int32_t Tq, int32_t H, int32_t d);
+int rr_user_token_attn_plan(const int32_t* key_offsets, const int32_t* query_offsets, int32_t B, int32_t Tk,
+                            int32_t Tq, int32_t H, int32_t d, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+int rr_user_token_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t Tk,
+                           int32_t Tq, int32_t H, int32_t d, int dtype, float scale, const void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace rr_ranker_cached_fwd needs (0 on unsupported sizes). */
 size_t rr_ranker_cached_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d);

@@ -299,6 +299,48 @@ int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_
                           scale, workspace, workspace_bytes, stream);
 }
 
+size_t rr_user_token_attn_workspace_bytes(int32_t B, int32_t Tk, int32_t Tq, int32_t H, int32_t d) {
+  return rr_cand_only_workspace_bytes(B, Tk, Tq, H, d);
+}
+
+int rr_user_token_attn_plan(const int32_t* key_offsets, const int32_t* query_offsets, int32_t B, int32_t Tk,
+                            int32_t Tq, int32_t H, int32_t d, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, Tk, Tq, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || Tq == 0 || H == 0) return RR_OK;
+  if (!key_offsets || !query_offsets) return RR_EINVAL;
+  const WsLayout w = ws_layout(B, 0, Tq, H);
+  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
+  const Ws p = carve_all(workspace, w);
+  const int bm = tile_rows(dtype, d, B, Tq);
+  const int64_t cap = attn_grid(B, Tq, H, bm);
+  return status_of(launch_worklist(2, key_offsets, query_offsets, 0, B, H, bm, Tq, Tk, static_cast<int>(cap),
+                                   p.meta, p.start, p.items, p.header, stream));
+}
+
+int rr_user_token_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t Tk,
+                           int32_t Tq, int32_t H, int32_t d, int dtype, float scale, const void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, Tk, Tq, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || Tq == 0 || H == 0) return RR_OK;
+  if (!q || !o || (Tk > 0 && (!k || !v))) return RR_EINVAL;
+  const WsLayout w = ws_layout(B, 0, Tq, H);
+  if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
+  const Ws p = carve_all(const_cast<void*>(workspace), w);
+  AttnArgs a{};
+  a.q = q;
+  a.k = Tk > 0 ? k : q;      // with no keys every row's list is empty; never read then
+  a.v = Tk > 0 ? v : q;
+  a.k_self = q; a.v_self = q;   // in bounds for every query row; no self-term is taken
+  a.o = o;
+  a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
+  a.B = B; a.H = H; a.mode = 2; a.rows = Tq;
+  a.scale_log2 = softmax_scale_log2(scale, d);
+  return run_attention(a, dtype, d, tile_rows(dtype, d, B, Tq), Tq, stream);
+}
+
 int rr_rope_positions(const int32_t* offsets, const int32_t* cand_start, const int32_t* pos_base,
                       int32_t B, int32_t T, int32_t* pos_out, hipStream_t stream) {
   if (B < 0 || T < 0) return RR_EINVAL;

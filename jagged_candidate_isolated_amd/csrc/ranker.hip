@@ -245,6 +245,52 @@ __global__ __launch_bounds__(256) void k_split_rows(const char* src, int64_t row
   }
 }
 
+// User-token rows: p[b] = min(max(user_tokens[b], 0), rows of user b's history block),
+// poff = their exclusive sums (one workgroup).
+__global__ __launch_bounds__(256) void k_prefix_offsets(const int32_t* user_tokens, const int32_t* hoff, int B,
+                                                        int32_t* poff) {
+  __shared__ int32_t sp[256];
+  const int tid = threadIdx.x;
+  int32_t carry = 0;
+  if (tid == 0) poff[0] = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    const int32_t x = b < B ? min(max(user_tokens[b], 0), max(hoff[b + 1] - hoff[b], 0)) : 0;
+    sp[tid] = x;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int32_t y = tid >= o ? sp[tid - o] : 0;
+      __syncthreads();
+      sp[tid] += y;
+      __syncthreads();
+    }
+    if (b < B) poff[b + 1] = carry + sp[tid];
+    carry += sp[255];
+    __syncthreads();
+  }
+}
+
+// Between the compact user-token rows (row j of user b: j in [poff[b], poff[b+1])) and
+// the first rows of each user's block in a blocked tensor (row block[b] + j - poff[b]):
+// gather (to_compact) or scatter.  Rows outside [0, n_compact) or [0, n_blocked) are
+// skipped.  One thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void k_prefix_rows(char* compact, char* blocked, int64_t row_bytes,
+                                                     const int32_t* block, const int32_t* poff, int B,
+                                                     int n_compact, int n_blocked, int to_compact) {
+  const int64_t chunks = row_bytes / 16, n = static_cast<int64_t>(n_compact) * chunks;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < n; e += int64_t(gridDim.x) * blockDim.x) {
+    const int j = static_cast<int>(e / chunks);
+    const int64_t c = e % chunks;
+    const int b = owner_of(poff, B, j);
+    const int64_t r = static_cast<int64_t>(block[b]) + j - poff[b];
+    if (j >= poff[b + 1] || r < 0 || r >= n_blocked) continue;
+    uint4* cp = reinterpret_cast<uint4*>(compact + static_cast<int64_t>(j) * row_bytes) + c;
+    uint4* bp = reinterpret_cast<uint4*>(blocked + r * row_bytes) + c;
+    if (to_compact) *cp = *bp;
+    else *bp = *cp;
+  }
+}
+
 int64_t grid_of(int64_t n, int64_t per) {
   const int64_t g = (n + per - 1) / per;
   return g < 1 ? 1 : (g > (int64_t(1) << 20) ? (int64_t(1) << 20) : g);
@@ -279,6 +325,24 @@ hipError_t launch_gemm_bt(const void* a, const void* w, int M, int N, int K, voi
   return res ? launch1(k_gemm_bt<1>, grid, 256, s, g) : launch1(k_gemm_bt<0>, grid, 256, s, g);
 }
 
+hipError_t launch_prefix_offsets(const int32_t* user_tokens, const int32_t* hoff, int B, int32_t* poff,
+                                 hipStream_t s) {
+  void* args[] = {&user_tokens, &hoff, &B, &poff};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k_prefix_offsets), dim3(1), dim3(256), args, 0, s);
+}
+
+hipError_t launch_prefix_rows(void* compact, void* blocked, int64_t row_bytes, const int32_t* block,
+                              const int32_t* poff, int B, int n_compact, int n_blocked, int to_compact,
+                              hipStream_t s) {
+  if (n_compact <= 0) return hipSuccess;
+  char* cp = static_cast<char*>(compact);
+  char* bp = static_cast<char*>(blocked);
+  void* args[] = {&cp, &bp, &row_bytes, &block, &poff, &B, &n_compact, &n_blocked, &to_compact};
+  const int64_t grid = grid_of(static_cast<int64_t>(n_compact) * (row_bytes / 16), 256);
+  return hipLaunchKernel(reinterpret_cast<const void*>(k_prefix_rows), dim3(static_cast<unsigned>(grid)), dim3(256),
+                         args, 0, s);
+}
+
 hipError_t launch_split_offsets(const int32_t* offsets, const int32_t* cand_start, int B, int32_t* hoff,
                                 int32_t* coff, int32_t* hlen, hipStream_t s) {
   void* args[] = {&offsets, &cand_start, &B, &hoff, &coff, &hlen};
@@ -303,7 +367,7 @@ namespace {
 constexpr float kRmsEps = 1e-6f;
 
 struct RankerWs {
-  size_t h, q, k, v, o, kh, vh, xh, hoff, coff, hlen, attn, cand, total;
+  size_t h, q, k, v, o, kh, vh, xh, xp, hoff, coff, hlen, poff, attn, cand, utok, total;
 };
 
 // Workspace of a layer-stack call: normed rows h, q, k, v, o (bf16, `rows` rows), the
@@ -311,8 +375,8 @@ struct RankerWs {
 // the caller does not take them (`th_buf` rows each), the split offsets, and the two
 // attention plans (full layers over T rows; candidate-only over Th history and Tc
 // candidate rows).
-RankerWs ranker_layout(int64_t B, int64_t rows, int64_t th_buf, int64_t T, int64_t Th, int64_t Tc, int64_t H,
-                       int64_t d) {
+RankerWs ranker_layout(int64_t B, int64_t rows, int64_t th_buf, int64_t T, int64_t Th, int64_t Tc, int64_t Tp,
+                       int64_t H, int64_t d) {
   const int64_t D = H * d;
   RankerWs w{};
   size_t off = 0;
@@ -325,31 +389,37 @@ RankerWs ranker_layout(int64_t B, int64_t rows, int64_t th_buf, int64_t T, int64
   w.kh = take(2 * th_buf * D);
   w.vh = take(2 * th_buf * D);
   w.xh = take(4 * th_buf * D);
+  w.xp = take(4 * Tp * D);
   w.hoff = take(4 * (B + 1));
   w.coff = take(4 * (B + 1));
   w.hlen = take(4 * (B + 1));
+  w.poff = take(4 * (B + 1));
   w.attn = take(T > 0 ? rr_attn_workspace_bytes(static_cast<int32_t>(B), static_cast<int32_t>(T),
                                                  static_cast<int32_t>(H), static_cast<int32_t>(d))
                       : 0);
   w.cand = take(rr_cand_only_workspace_bytes(static_cast<int32_t>(B), static_cast<int32_t>(Th),
                                              static_cast<int32_t>(Tc), static_cast<int32_t>(H),
                                              static_cast<int32_t>(d)));
+  w.utok = take(Tp > 0 ? rr_user_token_attn_workspace_bytes(static_cast<int32_t>(B), static_cast<int32_t>(Th),
+                                                            static_cast<int32_t>(Tp), static_cast<int32_t>(H),
+                                                            static_cast<int32_t>(d))
+                       : 0);
   w.total = off;
   return w;
 }
 
 // the full request: T rows, Tc of them candidates
-RankerWs full_layout(int64_t B, int64_t T, int64_t Tc, int64_t H, int64_t d) {
-  return ranker_layout(B, T, T - Tc, T, T - Tc, Tc, H, d);
+RankerWs full_layout(int64_t B, int64_t T, int64_t Tc, int64_t Tp, int64_t H, int64_t d) {
+  return ranker_layout(B, T, T - Tc, T, T - Tc, Tc, Tp, H, d);
 }
 
 // a cached request: Tc candidate rows against Th cached history rows
 RankerWs cached_layout(int64_t B, int64_t Th, int64_t Tc, int64_t H, int64_t d) {
-  return ranker_layout(B, Tc, 0, 0, Th, Tc, H, d);
+  return ranker_layout(B, Tc, 0, 0, Th, Tc, 0, H, d);
 }
 
-int ranker_sizes(int32_t B, int32_t T, int32_t Tc, int32_t H, int32_t d) {
-  if (B < 0 || T < 0 || Tc < 0 || Tc > T || H <= 0 || d <= 0) return RR_EINVAL;
+int ranker_sizes(int32_t B, int32_t T, int32_t Tc, int32_t H, int32_t d, int32_t Tp = 0) {
+  if (B < 0 || T < 0 || Tc < 0 || Tc > T || Tp < 0 || Tp > T - Tc || H <= 0 || d <= 0) return RR_EINVAL;
   if (!(d == 32 || d == 64 || d == 128)) return RR_EUNSUPPORTED;   // the bf16 MFMA attention
   const int64_t D = int64_t(H) * d;
   if (D % kGn != 0 || D > 16384) return RR_EUNSUPPORTED;           // projection tiles
@@ -407,9 +477,9 @@ using namespace rr;
 
 extern "C" {
 
-size_t rr_ranker_workspace_bytes(int32_t B, int32_t T, int32_t Tc, int32_t H, int32_t d) {
-  if (ranker_sizes(B, T, Tc, H, d) != RR_OK) return 0;
-  return full_layout(B, T, Tc, H, d).total;
+size_t rr_ranker_workspace_bytes(int32_t B, int32_t T, int32_t Tc, int32_t Tp, int32_t H, int32_t d) {
+  if (ranker_sizes(B, T, Tc, H, d, Tp) != RR_OK) return 0;
+  return full_layout(B, T, Tc, Tp, H, d).total;
 }
 
 int rr_rms_norm(const float* x, const float* gain, void* out, int32_t M, int32_t D, float eps,
@@ -431,14 +501,16 @@ int rr_linear(const void* a, const void* w, void* out, float* residual, int32_t 
 }
 
 int rr_ranker_fwd(float* x, const rr_layer* layers, int32_t n_layers, int32_t n_cand_only,
-                  const int32_t* offsets, const int32_t* cand_start, int32_t B, int32_t T, int32_t Tc,
-                  int32_t H, int32_t d, float theta_base, float* x_cand_out, float* x_hist_out,
-                  void* kv_cache, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  RR_TRY(ranker_sizes(B, T, Tc, H, d));
+                  const int32_t* offsets, const int32_t* cand_start, const int32_t* user_tokens, int32_t B,
+                  int32_t T, int32_t Tc, int32_t Tp, int32_t H, int32_t d, float theta_base, float* x_cand_out,
+                  float* x_hist_out, void* kv_cache, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (!user_tokens) Tp = 0;
+  RR_TRY(ranker_sizes(B, T, Tc, H, d, Tp));
   if (!layers_ok(layers, n_layers) || n_cand_only < 0 || n_cand_only > n_layers) return RR_EINVAL;
   if (B == 0 || T == 0) return RR_OK;
   if (!x || !offsets || !cand_start || (Tc > 0 && !x_cand_out)) return RR_EINVAL;
-  const RankerWs w = full_layout(B, T, Tc, H, d);
+  const RankerWs w = full_layout(B, T, Tc, Tp, H, d);
   if (!workspace || workspace_bytes < w.total) return RR_EWORKSPACE;
   const int32_t Th = T - Tc, D = H * d, n_full = n_layers - n_cand_only;
   const double lb = log2_theta(theta_base);
@@ -482,6 +554,18 @@ int rr_ranker_fwd(float* x, const rr_layer* layers, int32_t n_layers, int32_t n_
                               stream)));
   if (n_cand_only == 0) return RR_OK;
   RR_TRY(rr_cand_only_plan(hoff, coff, B, Th, Tc, H, d, RR_BF16, wc, wc_bytes, stream));
+  // candidate_only_layers_update_user_token: the user tokens (each user's first rows) keep
+  // being updated, reading the user's [user tokens | frozen history] keys; their states
+  // move to a compact block xp for the candidate-only layers
+  float* xp = at<float>(ws, w.xp);
+  int32_t* poff = at<int32_t>(ws, w.poff);
+  void* wu = at<void>(ws, w.utok);
+  const size_t wu_bytes = w.total - w.utok;
+  if (Tp > 0) {
+    RR_TRY(st(launch_prefix_offsets(user_tokens, hoff, B, poff, stream)));
+    RR_TRY(st(launch_prefix_rows(xp, xh, int64_t(D) * 4, hoff, poff, B, Tp, Th, 1, stream)));
+    RR_TRY(rr_user_token_attn_plan(hoff, poff, B, Th, Tp, H, d, RR_BF16, wu, wu_bytes, stream));
+  }
   for (int l = n_full; l < n_layers; ++l) {
     const rr_layer& L = layers[l];
     void* kh = cache ? static_cast<void*>(cache + (2 * l) * layer_elems) : at<void>(ws, w.kh);
@@ -492,10 +576,23 @@ int rr_ranker_fwd(float* x, const rr_layer* layers, int32_t n_layers, int32_t n_
     RR_TRY(st(launch_rms_norm(xh, L.norm_gain, h, Th, D, kRmsEps, stream)));
     RR_TRY(st(launch_gemm_bt(h, static_cast<const u16*>(L.w_qkv) + int64_t(D) * D, Th, 2 * D, D, kv, D,
                              nullptr, stream)));
+    if (Tp > 0) {   // the user tokens from their current states, into their key and value slots
+      RR_TRY(st(launch_rms_norm(xp, L.norm_gain, h, Tp, D, kRmsEps, stream)));
+      RR_TRY(st(launch_gemm_bt(h, L.w_qkv, Tp, 3 * D, D, qkv, D, nullptr, stream)));
+      RR_TRY(st(launch_prefix_rows(k, kh, int64_t(D) * 2, hoff, poff, B, Tp, Th, 0, stream)));
+      RR_TRY(st(launch_prefix_rows(v, vh, int64_t(D) * 2, hoff, poff, B, Tp, Th, 0, stream)));
+    }
     RR_TRY(st(launch_rope_qk(nullptr, kh, nullptr, kh, hoff, hoff + 1, nullptr, B, Th, H, d, RR_BF16, lb,
                              stream)));
+    if (Tp > 0) {   // user tokens at positions 0 .. p_b - 1, reading [user tokens | history]
+      RR_TRY(st(launch_rope_qk(q, nullptr, q, nullptr, poff, poff + 1, nullptr, B, Tp, H, d, RR_BF16, lb,
+                               stream)));
+      RR_TRY(rr_user_token_attn_run(q, kh, vh, o, B, Th, Tp, H, d, RR_BF16, 0.f, wu, wu_bytes, stream));
+      RR_TRY(st(launch_gemm_bt(o, L.w_o, Tp, D, D, nullptr, 0, xp, stream)));
+    }
     RR_TRY(cand_layer(x_cand_out, L, kh, vh, coff, hlen, B, Th, Tc, H, d, lb, ws, w, wc, wc_bytes, stream));
   }
+  if (Tp > 0) RR_TRY(st(launch_prefix_rows(xp, xh, int64_t(D) * 4, hoff, poff, B, Tp, Th, 0, stream)));
   return RR_OK;
 }
 

@@ -38,6 +38,7 @@ __device__ __forceinline__ int cost_bucket(int cost) {
 struct WorklistParams {
   int mode;              // 0: full sequence (offs_a = offsets, offs_b = cand_start)
                          // 1: candidate-only (offs_a = hist_offsets, offs_b = cand_offsets)
+                         // 2: as 1 with no self-term (user-token rows: offs_b = their offsets)
   const int32_t* offs_a;
   const int32_t* offs_b;
   int meta_ready;        // meta[] already written by the compaction prologue
@@ -82,7 +83,7 @@ __device__ __forceinline__ UserMeta plain_meta(const WorklistParams& p, int b) {
     m.n_q = ch - cl;
     m.kv_begin = hl;
     m.n_kv = hh - hl;
-    m.cand_rel = 0;
+    m.cand_rel = p.mode == 2 ? m.n_q : 0;   // mode 2: no query reads its own row
   }
   return m;
 }

@@ -47,9 +47,14 @@ _SIGS = {
                                    _I, _I, ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "rr_rms_norm": (ctypes.c_int, [_P, _P, _P, _I, _I, ctypes.c_float, _P]),
     "rr_linear": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P]),
-    "rr_ranker_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
-    "rr_ranker_fwd": (ctypes.c_int, [_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P,
-                                     _P, ctypes.c_size_t, _P]),
+    "rr_ranker_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "rr_ranker_fwd": (ctypes.c_int, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "rr_user_token_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "rr_user_token_attn_plan": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P, ctypes.c_size_t,
+                                               _P]),
+    "rr_user_token_attn_run": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float,
+                                              _P, ctypes.c_size_t, _P]),
     "rr_ranker_cached_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "rr_ranker_cached_fwd": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                             ctypes.c_size_t, _P]),
@@ -507,9 +512,11 @@ def _layer_array(layers, D, dev):
 
 def rr_ranker_fwd(x, layers, n_cand_only, offsets, cand_start, Tc: int, H: int, d: int, theta_base=None,
                   keep_cache=True, x_cand_out=None, x_hist_out=None, kv_cache=None, workspace=None,
-                  stream=None):
+                  stream=None, user_tokens=None, Tp: int = 0):
     """The layer stack over x float32 [T, H*d] (updated in place by the full layers).
     ``layers``: list of (norm_gain float32 [D], w_qkv bf16 [3D, D], w_o bf16 [D, D]).
+    ``user_tokens`` (int32 [B] on the device, Tp = their sum): the user tokens keep being
+    updated in the candidate-only layers.
     Returns (x_cand [Tc, D], x_hist [T-Tc, D], kv_cache bf16 [L, 2, T-Tc, H, d] or None)."""
     dev = x.device
     _need(x, "x", torch.float32)
@@ -533,11 +540,17 @@ def rr_ranker_fwd(x, layers, n_cand_only, offsets, cand_start, Tc: int, H: int, 
         _need(kv_cache, "kv_cache", torch.bfloat16, dev)
         if kv_cache.numel() != len(layers) * 2 * Th * D:
             raise ValueError("kv_cache must be [n_layers, 2, T - Tc, H, d]")
-    ws = _workspace(int(_lib.rr_ranker_workspace_bytes(B, T, Tc, H, d)), workspace, dev)
+    if user_tokens is not None:
+        _need(user_tokens, "user_tokens", torch.int32, dev)
+        if user_tokens.numel() != B:
+            raise ValueError("user_tokens must have B entries")
+    else:
+        Tp = 0
+    ws = _workspace(int(_lib.rr_ranker_workspace_bytes(B, T, Tc, Tp, H, d)), workspace, dev)
     _check("rr_ranker_fwd", _lib.rr_ranker_fwd(
         _ptr(x), ctypes.cast(arr, ctypes.c_void_p), len(layers), int(n_cand_only), _ptr(offsets),
-        _ptr(cand_start), B, T, Tc, H, d, float(theta_base or 0.0), _ptr(x_cand_out), _ptr(x_hist_out),
-        _ptr(kv_cache), _ptr(ws), ws.numel(), _stream(stream, dev)))
+        _ptr(cand_start), _ptr(user_tokens), B, T, Tc, int(Tp), H, d, float(theta_base or 0.0),
+        _ptr(x_cand_out), _ptr(x_hist_out), _ptr(kv_cache), _ptr(ws), ws.numel(), _stream(stream, dev)))
     return x_cand_out, x_hist_out, kv_cache
 
 
@@ -564,8 +577,33 @@ def rr_ranker_cached_fwd(x_cand, layers, kv_cache, hist_offsets, cand_offsets, H
     return x_cand
 
 
-def rr_ranker_workspace_bytes(B: int, T: int, Tc: int, H: int, d: int) -> int:
-    return int(_lib.rr_ranker_workspace_bytes(B, T, Tc, H, d))
+def rr_ranker_workspace_bytes(B: int, T: int, Tc: int, H: int, d: int, Tp: int = 0) -> int:
+    return int(_lib.rr_ranker_workspace_bytes(B, T, Tc, Tp, H, d))
+
+
+def rr_user_token_attn(q, k, v, key_offsets, query_offsets, scale=None, out=None, workspace=None,
+                       stream=None) -> torch.Tensor:
+    """Every query row of user b reads exactly user b's key rows (no self-term).
+    q [Tq, H, d]; k, v [Tk, H, d]; key_offsets, query_offsets int32 [B+1]."""
+    dev = q.device
+    _need(q, "q")
+    dt = _rr_dtype(q)
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(key_offsets, "key_offsets", torch.int32, dev)
+    _need(query_offsets, "query_offsets", torch.int32, dev)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    B = query_offsets.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    ws = _workspace(int(_lib.rr_user_token_attn_workspace_bytes(B, Tk, Tq, H, d)), workspace, dev)
+    _check("rr_user_token_attn_plan", _lib.rr_user_token_attn_plan(
+        _ptr(key_offsets), _ptr(query_offsets), B, Tk, Tq, H, d, dt, _ptr(ws), ws.numel(), _stream(stream, dev)))
+    _check("rr_user_token_attn_run", _lib.rr_user_token_attn_run(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Tk, Tq, H, d, dt, float(scale or 0.0), _ptr(ws), ws.numel(),
+        _stream(stream, dev)))
+    return out
 
 
 def rr_ranker_cached_workspace_bytes(B: int, Th: int, Tc: int, H: int, d: int) -> int:

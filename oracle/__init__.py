@@ -43,6 +43,7 @@ from .rotary import (  # noqa: F401
 )
 from .backward import full_attention_backward, attention_lse, gradient_error_scale  # noqa: F401
 from .ranker import (  # noqa: F401
-    Layer, rms_norm, block_full, block_cand_only, history_kv, split_history_and_candidates,
+    Layer, rms_norm, block_full, block_cand_only, block_user_token_layer, history_kv,
+    split_history_and_candidates,
     ranker_forward, ranker_forward_cached,
 )

@@ -111,7 +111,7 @@ def split_history_and_candidates(x, offsets, cand_start):
     return x[hidx], x[cidx], hoff, coff
 
 
-def _user_token_layer(x_p, x_h, x_c, layer, p, hist_offsets, cand_offsets, H, d, base, scale):
+def block_user_token_layer(x_p, x_h, x_c, layer, p, hist_offsets, cand_offsets, H, d, base, scale):
     """One candidate-only layer that also updates the user tokens: the full layer over each
     user's [prefix x_p | frozen history x_h | candidates x_c], history rows put back.
     p[b] = user b's prefix rows, the first p[b] rows of its block in hist_offsets (those of
@@ -171,7 +171,7 @@ def ranker_forward(x, layers, n_cand_only, offsets, cand_start, H, d, base=DEFAU
     p = np.asarray(user_tokens, np.int64)
     x_p = np.concatenate([x_hist[hoff[b]:hoff[b] + p[b]] for b in range(len(p))] + [np.zeros((0, x.shape[1]))])
     for layer in layers[n_full:]:
-        x_p, x_cand, kh, vh = _user_token_layer(x_p, x_hist, x_cand, layer, p, hoff, coff, H, d, base, scale)
+        x_p, x_cand, kh, vh = block_user_token_layer(x_p, x_hist, x_cand, layer, p, hoff, coff, H, d, base, scale)
         cache.append((kh, vh))
     poff = np.concatenate([[0], np.cumsum(p)])
     x_hist = x_hist.copy()

@@ -181,8 +181,9 @@ def test_ranker_argument_errors():
                  ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return lib.rr_ranker_fwd(a["x"], ctypes.cast(a["layers"], ctypes.c_void_p) if a["layers"] else None,
-                                 a["n"], a["nco"], a["off"], a["cs"], a["B"], a["T"], a["Tc"], a["H"], a["d"], 0.0,
-                                 a["xc"], None, None, a["ws"], a["ws_bytes"], None)
+                                 a["n"], a["nco"], a["off"], a["cs"], a.get("ut"), a["B"], a["T"], a["Tc"],
+                                 a.get("Tp", 0), a["H"], a["d"], 0.0, a["xc"], None, None, a["ws"], a["ws_bytes"],
+                                 None)
     assert call(d=16) == rr.RR_EUNSUPPORTED                 # the MFMA attention: d 32, 64, 128
     assert call(H=3) == rr.RR_EUNSUPPORTED                  # D = 192 is not a multiple of 128
     assert call(Tc=101) == rr.RR_EINVAL
@@ -192,11 +193,15 @@ def test_ranker_argument_errors():
     assert call(x=None) == rr.RR_EINVAL
     assert call(xc=None) == rr.RR_EINVAL
     assert call(ws=None) == rr.RR_EWORKSPACE
-    need = lib.rr_ranker_workspace_bytes(2, 100, 10, 4, 64)
+    assert call(ut=FAKE, Tp=91) == rr.RR_EINVAL             # more user tokens than rows before candidates
+    assert call(ut=FAKE, Tp=-1) == rr.RR_EINVAL
+    assert call(ut=None, Tp=-1, ws=None) == rr.RR_EWORKSPACE   # Tp is ignored without user tokens
+    assert lib.rr_ranker_workspace_bytes(2, 100, 10, 8, 4, 64) > lib.rr_ranker_workspace_bytes(2, 100, 10, 0, 4, 64)
+    need = lib.rr_ranker_workspace_bytes(2, 100, 10, 0, 4, 64)
     assert need > lib.rr_attn_workspace_bytes(2, 100, 4, 64)
     assert call(ws_bytes=need - 1) == rr.RR_EWORKSPACE
     assert call(B=0, x=None, ws=None) == rr.RR_OK
-    assert lib.rr_ranker_workspace_bytes(2, 100, 10, 4, 16) == 0
+    assert lib.rr_ranker_workspace_bytes(2, 100, 10, 0, 4, 16) == 0
     assert lib.rr_ranker_cached_workspace_bytes(2, 90, 10, 4, 64) > 0
     assert lib.rr_ranker_cached_fwd(None, ctypes.cast(arr, ctypes.c_void_p), 2, FAKE, FAKE, FAKE, 2, 90, 10, 4, 64,
                                     0.0, FAKE, 1 << 40, None) == rr.RR_EINVAL
@@ -204,6 +209,11 @@ def test_ranker_argument_errors():
     assert lib.rr_linear(FAKE, FAKE, FAKE, None, 10, 128, 48, None) == rr.RR_EUNSUPPORTED   # K % 64
     assert lib.rr_linear(FAKE, FAKE, FAKE, FAKE, 10, 128, 64, None) == rr.RR_EINVAL          # both outputs
     assert lib.rr_rms_norm(FAKE, FAKE, FAKE, 3, 6, 0.0, None) == rr.RR_EINVAL                # D % 4
+    assert lib.rr_user_token_attn_plan(None, FAKE, 2, 10, 4, 2, 64, 1, FAKE, 1 << 30, None) == rr.RR_EINVAL
+    assert lib.rr_user_token_attn_run(None, FAKE, FAKE, FAKE, 2, 10, 4, 2, 64, 1, 0.0, FAKE, 1 << 30,
+                                      None) == rr.RR_EINVAL
+    assert lib.rr_user_token_attn_run(FAKE, FAKE, FAKE, FAKE, 2, 10, 4, 2, 64, 1, 0.0, None, 0,
+                                      None) == rr.RR_EWORKSPACE
 
 
 def test_workspace_size_grows_with_work():

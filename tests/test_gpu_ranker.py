@@ -41,10 +41,13 @@ def _setup(H, d, n_layers, seed, shapes=SHAPES):
     return x, off, cs, dev_layers, or_layers
 
 
-def _run(x, off, cs, dev_layers, n_cand_only, H, d):
+def _run(x, off, cs, dev_layers, n_cand_only, H, d, user_tokens=None):
     Tc = int((off[1:] - cs).sum())
     xd = to_dev(x.copy())
-    xc, xh, cache = rr().rr_ranker_fwd(xd, dev_layers, n_cand_only, to_dev(off), to_dev(cs), Tc, H, d)
+    ut = None if user_tokens is None else to_dev(np.asarray(user_tokens, np.int32))
+    Tp = 0 if user_tokens is None else int(np.sum(user_tokens))
+    xc, xh, cache = rr().rr_ranker_fwd(xd, dev_layers, n_cand_only, to_dev(off), to_dev(cs), Tc, H, d,
+                                       user_tokens=ut, Tp=Tp)
     torch.cuda.synchronize()
     return xd, xc, xh, cache
 
@@ -203,3 +206,72 @@ def test_candidate_order_bit_identical():
     cperm[coff[b]:coff[b + 1]] = coff[b] + (perm[cs[b]:off[b + 1]] - cs[b])
     assert torch.equal(xh2, xh)
     assert torch.equal(xc2, xc[to_dev(cperm)])
+
+
+def test_user_token_attention():
+    """rr_user_token_attn: each query of a user reads exactly that user's keys, no self-term;
+    a user without keys gives 0; against the oracle's masked softmax attention."""
+    from oracle.attention import masked_softmax_attention
+    rng = np.random.default_rng(80)
+    H, d = 3, 64
+    nk, nq = np.array([5, 0, 300, 1, 70]), np.array([2, 3, 0, 4, 9])
+    koff = np.concatenate([[0], np.cumsum(nk)]).astype(np.int32)
+    qoff = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q, k, v = (W.round_to_bf16(rng.standard_normal((n, H, d)).astype(np.float32)) for n in (qoff[-1], koff[-1],
+                                                                                          koff[-1]))
+    got = _np(rr().rr_user_token_attn(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
+                                      to_dev(v, torch.bfloat16), to_dev(koff), to_dev(qoff)))
+    ref = np.zeros(q.shape)
+    for b in range(len(nk)):
+        qs, ks = slice(qoff[b], qoff[b + 1]), slice(koff[b], koff[b + 1])
+        if nk[b] == 0 or nq[b] == 0:
+            continue
+        for h in range(H):
+            ref[qs, h] = masked_softmax_attention(q[qs, h].astype(np.float64), k[ks, h].astype(np.float64),
+                                                  v[ks, h].astype(np.float64), np.ones((nq[b], nk[b]), bool),
+                                                  1.0 / np.sqrt(d))
+    from _gpu import assert_close
+    assert_close(got, ref, "bf16", "user-token attention")
+    assert not got[qoff[1]:qoff[2]].any(), "a user with no keys must give 0"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_user_token_layers_against_oracle(d):
+    """candidate_only_layers_update_user_token: each candidate-only layer's update of the
+    user tokens and of the candidates against the oracle's layer on the GPU's own state;
+    the other rows before the candidate start stay frozen bit for bit."""
+    H, n_layers, n_cand_only = 4, 4, 2
+    x, off, cs, dl, ol = _setup(H, d, n_layers, seed=90 + d)
+    p = np.array(SHAPES["prefix"])
+    n_full = n_layers - n_cand_only
+    _, xc, xh, _ = _run(x, off, cs, dl[:n_full], 0, H, d)
+    prev_c, prev_h = _np(xc), _np(xh)
+    frozen_h = prev_h.copy()
+    hoff = np.concatenate([[0], np.cumsum(cs - off[:-1])])
+    coff = np.concatenate([[0], np.cumsum(off[1:] - cs)])
+    is_p = np.zeros(len(prev_h), bool)
+    for b in range(len(p)):
+        is_p[hoff[b]:hoff[b] + p[b]] = True
+    for l in range(n_full + 1, n_layers + 1):
+        _, xc, xh, _ = _run(x, off, cs, dl[:l], l - n_full, H, d, user_tokens=p)
+        got_c, got_h = _np(xc), _np(xh)
+        assert np.array_equal(got_h[~is_p], frozen_h[~is_p]), "a history row moved"
+        ref_p, ref_c, _, _ = RK.block_user_token_layer(prev_h[is_p], frozen_h, prev_c, ol[l - 1], p, hoff, coff,
+                                                       H, d, 10000.0, None)
+        _frob(got_c, ref_c, prev_c, f"candidates, layer {l}")
+        _frob(got_h[is_p], ref_p, prev_h[is_p], f"user tokens, layer {l}")
+        prev_c, prev_h = got_c, got_h
+
+
+def test_user_token_cached_request_bit_identical():
+    H, d, n_layers, nco = 4, 64, 4, 2
+    x, off, cs, dl, _ = _setup(H, d, n_layers, seed=95)
+    p = np.array(SHAPES["prefix"])
+    _, xc, xh, cache = _run(x, off, cs, dl, nco, H, d, user_tokens=p)
+    _, xc_plain, xh_plain, _ = _run(x, off, cs, dl, nco, H, d)
+    assert not torch.equal(xc, xc_plain), "updating the user tokens changed nothing"
+    _, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    again = rr().rr_ranker_cached_fwd(to_dev(xc0.astype(np.float32)), dl, cache, to_dev(hoff.astype(np.int32)),
+                                      to_dev(coff.astype(np.int32)), H, d)
+    torch.cuda.synchronize()
+    assert torch.equal(again, xc)
