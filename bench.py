@@ -57,6 +57,9 @@ def parse_args():
                    help="a step is plan + forward with lse + backward (full-sequence bf16, d 64 or 128)")
     p.add_argument("--ranker", action="store_true",
                    help="the layer stack (6 full + 2 candidate-only layers) end to end; candidates/s")
+    p.add_argument("--update-user-token", action="store_true",
+                   help="with --ranker: the prefix rows (user tokens) keep being updated in the "
+                        "candidate-only layers")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -356,10 +359,17 @@ def run_ranker(args, b, torch, rr):
     xc2 = torch.empty_like(xc_src)
     ws2 = torch.empty(rr.rr_ranker_cached_workspace_bytes(b.B, Th, Tc, b.H, b.d), dtype=torch.uint8, device=dev)
 
+    ut, Tp = None, 0
+    if args.update_user_token:
+        ut = torch.from_numpy(b.prefix.astype(np.int32)).to(dev)
+        Tp = int(b.prefix.sum())
+        ws = torch.empty(rr.rr_ranker_workspace_bytes(b.B, b.T, Tc, b.H, b.d, Tp=Tp), dtype=torch.uint8,
+                         device=dev)
+
     def full_step():
         x.copy_(x_src)
         rr.rr_ranker_fwd(x, dl, RANKER_CAND_ONLY, off, cst, Tc, b.H, b.d, x_cand_out=xc, x_hist_out=xh,
-                         kv_cache=cache, workspace=ws)
+                         kv_cache=cache, workspace=ws, user_tokens=ut, Tp=Tp)
 
     def cached_step():
         xc2.copy_(xc_src)
@@ -398,7 +408,7 @@ def run_ranker(args, b, torch, rr):
         "ms_per_step": ms_full, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (random projections)",
         "config": dict(describe(args.config, b), parallelism="none (1 GPU)", layers=RANKER_LAYERS,
-                       cand_only_layers=RANKER_CAND_ONLY, D=D,
+                       cand_only_layers=RANKER_CAND_ONLY, D=D, update_user_token=bool(args.update_user_token),
                        step="copy of the input states + rr_ranker_fwd (kv cache written)"),
         "ranker": {
             "full_request": {"ms": ms_full, "candidates_per_s": Tc / (ms_full / 1e3),
@@ -411,11 +421,12 @@ def run_ranker(args, b, torch, rr):
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = ranker_cpu_baseline(b, x0, layers, args.cpu_seconds)
+        out["cpu_baseline"] = ranker_cpu_baseline(b, x0, layers, args.cpu_seconds,
+                                                  user_tokens=b.prefix if args.update_user_token else None)
     print(json.dumps(out), flush=True)
 
 
-def ranker_cpu_baseline(b, x0, layers, budget_s):
+def ranker_cpu_baseline(b, x0, layers, budget_s, user_tokens=None):
     """The oracle's layer stack on the first users of the batch, one user at a time, until
     about ``budget_s`` of CPU time; candidates/s."""
     import numpy as np
@@ -430,7 +441,8 @@ def ranker_cpu_baseline(b, x0, layers, budget_s):
     users = cands = 0
     while time.perf_counter() - t0 < budget_s and users < b.B:
         lo, cs, hi = int(b.offsets[users]), int(b.cand_start[users]), int(b.offsets[users + 1])
-        RK.ranker_forward(x0[lo:hi], ol, RANKER_CAND_ONLY, [0, hi - lo], [cs - lo], b.H, b.d)
+        RK.ranker_forward(x0[lo:hi], ol, RANKER_CAND_ONLY, [0, hi - lo], [cs - lo], b.H, b.d,
+                          user_tokens=None if user_tokens is None else user_tokens[users:users + 1])
         cands += hi - cs
         users += 1
     dt = time.perf_counter() - t0

@@ -319,7 +319,7 @@ hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
 #define RR_NARROW_STAGES 2
 #endif
 #ifndef RR_NARROW_BN64
-#define RR_NARROW_BN64 128
+#define RR_NARROW_BN64 64
 #endif
 #ifndef RR_NARROW_BN128
 #define RR_NARROW_BN128 64
@@ -328,7 +328,7 @@ hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
 #define RR_WIDE_STAGES 4
 #endif
 #ifndef RR_WIDE_BN64
-#define RR_WIDE_BN64 128
+#define RR_WIDE_BN64 64
 #endif
 #ifndef RR_WIDE_BN128
 #define RR_WIDE_BN128 64
