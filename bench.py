@@ -3,8 +3,9 @@
 
 A step is one pass of the hot path over one batch with its inputs resident in HBM:
 ``rr_attn_plan`` (segment IDs / bounds / length-sorted work list) then ``rr_attn_run``
-(the fused attention kernel) -- or, for the candidate-only workload,
-``rr_cand_only_plan`` + ``rr_cand_only_run``.  The default workload is the
+(the fused attention kernel) -- or, for a small unpadded batch such as the default
+workload, ``rr_attn_fwd``, whose attention kernel builds the work list itself (one
+launch); for the candidate-only workload ``rr_cand_only_plan`` + ``rr_cand_only_run``.  The default workload is the
 short-history batch (B=64, prefix 4, history log-uniform in [10, 1000], 32
 candidates per user, H=4, d=64, bf16).  Steps rotate over enough copies of the
 inputs (>= 1 GiB in total) that no step finds its data in the 256 MB Infinity Cache.
@@ -149,6 +150,18 @@ def work_counts(cfg, b):
             acc.full_mode_bytes(b.T, b.H, b.d, es), int(b.cand.sum()))
 
 
+def self_planned(b) -> bool:
+    """Whether rr_attn_fwd plans this batch inside the attention kernel (a small unpadded
+    bf16 batch: at most 256 users, at most 1024 workgroups); the library's rule."""
+    if b.valid is not None or b.dtype != "bf16" or b.d < 32:
+        return False
+    bm = 256 if b.T >= 2048 * b.B else 128
+    q = 64
+    grid = (b.H + 1) * ((b.T + bm - 1) // bm + b.B)
+    grid = (grid + q - 1) // q * q
+    return b.B <= 256 and b.B <= 2 * bm and grid <= 1024
+
+
 def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
     """Device copies of the inputs (rotated), outputs, the workspace and the step calls:
     plan(), run(i) (with the rotary encoding first when ``rope``; forward with lse and then
@@ -187,7 +200,7 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
 
     # rotary q / k land in one set of buffers that the attention of the same step reads
     rot = [torch.empty_like(t) for t in base] if rope else None
-    bwd_only = None
+    bwd_only = rope_only = None
     if cfg == 4:
         hist_len = (hoff[1:] - hoff[:-1]).contiguous()
         hist_end, cand_first = hoff[1:].contiguous(), coff[:-1].contiguous()
@@ -207,6 +220,15 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
                 rr.rr_cand_only_run(rot[0], rot[1], s[2], rot[3], s[4], b.B, ws, out=outs[i % copies])
             else:
                 rr.rr_cand_only_run(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies])
+    elif self_planned(b) and not rope and not backward:
+        # the library plans inside the attention kernel for such a batch: one launch a step
+        def plan():
+            pass
+
+        def run(i):
+            s = sets[i % copies]
+            rr.rr_attn_fwd(s[0], s[1], s[2], off, cst, valid, b.attend_padded_history, out=outs[i % copies],
+                           workspace=ws)
     else:
         def plan():
             rr.rr_attn_plan(off, cst, b.T, b.H, b.d, dt, valid=valid,
@@ -583,6 +605,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(b.name)
     roof["kernel"] = "k_attn_mfma" if b.dtype == "bf16" and b.d >= 32 else "k_attn_simple"
+    roof["self_planned"] = bool(cfg != 4 and self_planned(b) and not args.rope and not args.backward)
     roof["kernel_ms"] = kernel_ms
     roof["alg_bytes"] = alg_bytes
     roof["alg_flops"] = exec_flops

@@ -232,6 +232,17 @@ int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int3
   if (st != RR_OK) return st;
   if (B == 0 || T == 0 || H == 0) return RR_OK;
   if (!q || !k || !v || !o) return RR_EINVAL;
+  const int bm = tile_rows(dtype, d, B, T);
+  const int64_t grid = attn_grid(B, T, H, bm);
+  if (!valid && use_mfma(dtype, d) && B <= kSelfPlanUsers && B <= 2 * bm && grid <= kSelfPlanGrid) {
+    // a small unpadded batch: every workgroup plans for itself, no planning launch
+    if (!offsets || !cand_start) return RR_EINVAL;
+    if (!workspace || workspace_bytes < ws_layout(B, T, T, H).total) return RR_EWORKSPACE;
+    AttnArgs a = full_args(q, k, v, o, B, T, H, d, scale, workspace);
+    a.offsets = offsets;
+    a.cand_start = cand_start;
+    return status_of(launch_attn_mfma_self_planned(a, d, bm, grid, stream));
+  }
   const int r = rr_attn_plan(offsets, cand_start, valid, attend_padded_history, B, T, H, d, dtype,
                              workspace, workspace_bytes, stream);
   if (r != RR_OK) return r;

@@ -26,9 +26,10 @@
 //
 // Pipeline.  K and V tiles go to LDS by direct-to-LDS loads (no register staging)
 // into NS rotating buffers, NS-1 tiles ahead of the tile being computed; one
-// barrier per tile.  This kernel takes the short users (four waves, 128 query rows,
-// two stages, two workgroups per CU); long users go to the two-block kernel in
-// attn_pp.hip.
+// barrier per tile.  Two tile shapes: narrow (four waves, 128 query rows, two stages,
+// two workgroups per CU) and wide (eight waves, 256 query rows, four stages, one
+// workgroup per CU) for batches of long users.  A small unpadded batch can skip the
+// planning kernel: each workgroup then builds the work list itself (self_plan_item).
 //
 // Numerics: bf16 operands, fp32 accumulation, online softmax in fp32 with exp2
 // (scale * log2 e folded into one FMA), P rounded to bf16 for the PV product,
@@ -285,7 +286,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   }
 }
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, bool SELF>
 __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   // pipeline stages (stages past NS are never referenced and take no LDS)
   __shared__ __attribute__((aligned(16))) u16 k0[BN * D], k1[BN * D], k2[BN * D], k3[BN * D];
@@ -293,7 +294,14 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   const Stages st{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
   int2 it;
   UserMeta um;
-  bool indexed;
+  bool indexed = false;
+  if constexpr (SELF) {   // an unpadded batch planned in this workgroup
+    __shared__ SelfPlanLds sp;
+    if (!self_plan_item(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, xcd_item(blockIdx.x), sp, it, um))
+      return;
+    attn_item<D, BN, NW, NS, false>(a, it, um, false, st);
+    return;
+  }
   if (!fetch_item(a, NW * kQw, xcd_item(blockIdx.x), it, um, indexed)) return;
   if (item_head(it) == kZeroHead) {
     zero_padding_tile(a, um, item_tile(it), NW * kQw, a.H * D * 2, threadIdx.x, NW * 64);
@@ -306,9 +314,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     attn_item<D, BN, NW, NS, false>(a, it, um, indexed, st);
 }
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, bool SELF = false>
 hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
-  return launch1(k_attn_mfma<D, BN, NW, NS>, grid, NW * 64, s, a);
+  return launch1(k_attn_mfma<D, BN, NW, NS, SELF>, grid, NW * 64, s, a);
 }
 
 }  // namespace
@@ -334,23 +342,39 @@ hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
 #define RR_WIDE_BN128 64
 #endif
 
-hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s) {
+namespace {
+
+template <bool SELF>
+hipError_t launch_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s) {
   if (bm == kBmMfmaWide) {
     constexpr int NW = kBmMfmaWide / kQw, NS = RR_WIDE_STAGES;
     switch (d) {
-      case 32: return go<32, 128, NW, NS>(a, grid, s);
-      case 64: return go<64, RR_WIDE_BN64, NW, NS>(a, grid, s);
-      case 128: return go<128, RR_WIDE_BN128, NW, NS>(a, grid, s);
+      case 32: return go<32, 128, NW, NS, SELF>(a, grid, s);
+      case 64: return go<64, RR_WIDE_BN64, NW, NS, SELF>(a, grid, s);
+      case 128: return go<128, RR_WIDE_BN128, NW, NS, SELF>(a, grid, s);
       default: return hipErrorInvalidValue;
     }
   }
   constexpr int NW = kBmMfmaNarrow / kQw, NS = RR_NARROW_STAGES;
   switch (d) {
-    case 32: return go<32, 128, NW, NS>(a, grid, s);
-    case 64: return go<64, RR_NARROW_BN64, NW, NS>(a, grid, s);
-    case 128: return go<128, RR_NARROW_BN128, NW, NS>(a, grid, s);
+    case 32: return go<32, 128, NW, NS, SELF>(a, grid, s);
+    case 64: return go<64, RR_NARROW_BN64, NW, NS, SELF>(a, grid, s);
+    case 128: return go<128, RR_NARROW_BN128, NW, NS, SELF>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s) {
+  return launch_mfma<false>(a, d, bm, grid, s);
+}
+
+// The batch's offsets and cand_start in a.offsets / a.cand_start, no plan: a.B <=
+// kSelfPlanUsers (and <= the workgroup size, 2 bm) and grid <= kSelfPlanGrid.
+hipError_t launch_attn_mfma_self_planned(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s) {
+  if (a.B > kSelfPlanUsers || a.B > 2 * bm || grid > kSelfPlanGrid) return hipErrorInvalidValue;
+  return launch_mfma<true>(a, d, bm, grid, s);
 }
 
 }  // namespace rr

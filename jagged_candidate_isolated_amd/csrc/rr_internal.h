@@ -127,6 +127,8 @@ struct AttnArgs {
   const int32_t* idx;  // row lists (used when plan->indexed)
   float scale_log2;    // softmax scale * log2(e)
   float* lse;          // [rows][H] natural-log sum of exp(scale q.k) over each row's keys, or NULL
+  const int32_t* offsets;     // self-planned launches only: the batch's offsets and cand_start
+  const int32_t* cand_start;
 };
 
 // The work item of workgroup slot `item` and its user: false when the plan in the
@@ -158,6 +160,128 @@ __device__ __forceinline__ int8_t segment_of(int row, int cand_start, const uint
   return ok ? (is_candidate ? int8_t(-1) : int8_t(1)) : int8_t(0);
 }
 
+constexpr int kBuckets = 128;      // logarithmic key-count buckets of the work list's sort
+
+// Bucket of a key count, longest first: bucket 0 holds the largest counts and the
+// last bucket the users without keys.  Four buckets per octave.
+__device__ __forceinline__ int cost_bucket(int cost) {
+  if (cost <= 0) return kBuckets - 1;
+  const int lg = 31 - __clz(cost);                                   // 0..30
+  const int frac = lg >= 2 ? (cost >> (lg - 2)) & 3 : (cost << (2 - lg)) & 3;
+  return kBuckets - 2 - min(lg * 4 + frac, kBuckets - 2);            // 0..126
+}
+
+// Self-planned launches.  A small unpadded full-sequence batch (at most kSelfPlanUsers
+// users and a grid of at most kSelfPlanGrid workgroups) skips the separate planning
+// kernel: every workgroup rebuilds the work list in LDS from offsets and cand_start
+// and takes its own item.  The list is the planning kernel's (users by descending
+// key-count bucket, heads outer and query tiles inner within a user) with ties broken
+// by user index, so every workgroup builds the same one.  Worth it only when there are
+// about as many items as workgroup slots: then the planning launch is a large part of
+// the batch's latency, while each workgroup's own planning costs a few microseconds
+// once rather than once per round of items.
+constexpr int kSelfPlanUsers = 256;
+constexpr int kSelfPlanGrid = 1024;
+
+struct SelfPlanLds {
+  int32_t lo[kSelfPlanUsers];
+  int32_t nq[kSelfPlanUsers];
+  int32_t nkv[kSelfPlanUsers];
+  int32_t order[kSelfPlanUsers];
+  int32_t start[kSelfPlanUsers + 1];
+  int32_t hist[kBuckets];
+  int32_t wave[16];
+  uint32_t bkt[kSelfPlanUsers / 4];   // one byte per user
+};
+
+// Item `item` of the batch (offsets, cand_start: B users over `rows` rows, H heads,
+// bm-row query tiles) into it / um; false past the last item.  blockDim.x >= B.
+__device__ __forceinline__ bool self_plan_item(const int32_t* offsets, const int32_t* cand_start, int B, int H,
+                                               int bm, int rows, int item, SelfPlanLds& s, int2& it,
+                                               UserMeta& um) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  for (int i = tid; i < kBuckets; i += blockDim.x) s.hist[i] = 0;
+  for (int i = tid; i < kSelfPlanUsers / 4; i += blockDim.x) s.bkt[i] = 0;
+  __syncthreads();
+  int bkt = kBuckets - 1, cnt = 0;
+  if (tid < B) {   // row ranges clamped into [0, rows), as the planning kernel does
+    const int lo = min(max(offsets[tid], 0), rows);
+    const int hi = min(max(offsets[tid + 1], lo), rows);
+    const int cs = min(max(cand_start[tid], lo), hi);
+    s.lo[tid] = lo;
+    s.nq[tid] = hi - lo;
+    s.nkv[tid] = cs - lo;
+    cnt = H * ((hi - lo + bm - 1) / bm);
+    bkt = cost_bucket(cs - lo);
+    atomicOr(&s.bkt[tid >> 2], static_cast<uint32_t>(bkt) << (8 * (tid & 3)));
+    atomicAdd(&s.hist[bkt], 1);
+  }
+  __syncthreads();
+  if (tid < 64) {   // exclusive offsets of the 128 buckets
+    const int a = s.hist[2 * tid], c = s.hist[2 * tid + 1];
+    int x = a + c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (tid >= off) x += y;
+    }
+    s.hist[2 * tid] = x - a - c;
+    s.hist[2 * tid + 1] = x - c;
+  }
+  __syncthreads();
+  if (tid < B) {   // stable rank: users before this one in its bucket, four bytes a read
+    int rank = s.hist[bkt];
+    const uint32_t pat = 0x01010101u * static_cast<uint32_t>(bkt);
+    for (int w = 0; w < (tid >> 2); ++w) {
+      const uint32_t x = s.bkt[w] ^ pat;   // zero bytes = same bucket
+      rank += __popc(~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x | 0x7f7f7f7fu));
+    }
+    for (int j = tid & ~3; j < tid; ++j) rank += ((s.bkt[j >> 2] >> (8 * (j & 3))) & 0xff) == static_cast<uint32_t>(bkt);
+    s.order[rank] = tid;
+  }
+  __syncthreads();
+  // exclusive scan of the item counts in that order (B <= blockDim.x: one pass)
+  int c = 0;
+  if (tid < B) {
+    const int u = s.order[tid];
+    c = H * ((s.nq[u] + bm - 1) / bm);
+  }
+  int x = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s.wave[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s.wave[w];
+  if (tid < B) s.start[tid] = before + x - c;
+  if (tid == 0) {
+    int total = 0;
+    for (int w = 0; w < nw; ++w) total += s.wave[w];
+    s.start[B] = total;
+  }
+  __syncthreads();
+  if (item >= s.start[B]) return false;
+  int lo = 0, hi = B;   // last r with start[r] <= item
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s.start[mid] <= item) lo = mid; else hi = mid;
+  }
+  const int u = s.order[lo];
+  const int nqt = (s.nq[u] + bm - 1) / bm, local = item - s.start[lo];
+  it = make_int2(u, ((local % nqt) << 10) | (local / nqt));
+  um = UserMeta{};
+  um.q_begin = s.lo[u];
+  um.n_q = s.nq[u];
+  um.kv_begin = s.lo[u];
+  um.n_kv = s.nkv[u];
+  um.cand_rel = s.nkv[u];
+  um.kv_direct = 1;
+  return true;
+}
+
 // Launch a kernel that takes one parameter struct; returns the launch status
 // (hipLaunchKernel reports it directly, so no sticky last-error is read or cleared).
 template <typename P>
@@ -185,6 +309,7 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
                            int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
+hipError_t launch_attn_mfma_self_planned(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dk,
                            void* dv, float* delta, float scale, int d, int bm, int64_t grid,
                            hipStream_t s);

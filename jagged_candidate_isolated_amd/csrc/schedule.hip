@@ -24,17 +24,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
-constexpr int kBuckets = 128;      // logarithmic key-count buckets of the counting sort
-
-// Bucket of a key count, longest first: bucket 0 holds the largest counts and the
-// last bucket the users without keys.  Four buckets per octave.
-__device__ __forceinline__ int cost_bucket(int cost) {
-  if (cost <= 0) return kBuckets - 1;
-  const int lg = 31 - __clz(cost);                                   // 0..30
-  const int frac = lg >= 2 ? (cost >> (lg - 2)) & 3 : (cost << (2 - lg)) & 3;
-  return kBuckets - 2 - min(lg * 4 + frac, kBuckets - 2);            // 0..126
-}
-
 struct WorklistParams {
   int mode;              // 0: full sequence (offs_a = offsets, offs_b = cand_start)
                          // 1: candidate-only (offs_a = hist_offsets, offs_b = cand_offsets)

@@ -248,3 +248,28 @@ def test_scale_argument():
     ref = A.full_attention(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, scale=0.37)
     assert_close(got, ref, "f32", "scale 0.37")
     assert math.isclose(0.37, 0.37)
+
+
+@pytest.mark.parametrize("cfg", [2, "ragged64", "ragged128"])
+def test_self_planned_equals_planned(cfg):
+    """rr_attn_fwd on a small unpadded batch builds the work list inside the attention
+    kernel; the outputs equal, bit for bit, those of the separate plan + run (and the
+    oracle, on config 2: test_config2_every_element)."""
+    from _gpu import rr
+    if cfg == 2:
+        fb = W.config2()
+    else:
+        d = 64 if cfg.endswith("64") else 128
+        rng = np.random.default_rng(d)
+        fb = W.make_full_batch(rng, "self-plan", prefix=[4, 0, 2, 0, 3], hist=[900, 0, 17, 0, 250],
+                               cand=[32, 5, 0, 0, 129], H=3, d=d, seed=9000 + d)
+    dev = full_dev(fb)
+    fused = run_full(fb, dev)
+    T, H, d = fb.q.shape
+    ws = rr().rr_attn_plan(dev["offsets"], dev["cand_start"], T, H, d, dev["q"].dtype)
+    out = rr().rr_attn_run(dev["q"], dev["k"], dev["v"], fb.B, ws)
+    torch.cuda.synchronize()
+    planned = out.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(fused, planned)
+    if cfg != 2:
+        assert_close(fused, _oracle_full(fb), "bf16", f"self-planned {cfg}")
