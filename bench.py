@@ -69,13 +69,18 @@ def parse_args():
     return p.parse_args()
 
 
+# the sources the forward attention step is built from: its kernel, the shared tile
+# helpers, the plan (work list and padded-row compaction) and the launch logic
+FORWARD_SOURCES = ("attn_mfma.hip", "mfma_tile.h", "rr_internal.h", "schedule.hip", "segments.hip", "api.hip")
+
+
 def source_hash() -> str:
-    """Digest of the kernel sources (and the ABI header): traffic counters taken on other
-    sources are not reported."""
+    """Digest of the forward attention step's sources (and the ABI header): traffic counters
+    taken on other sources are not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jagged_candidate_isolated_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "rr.h")]
+    files = [os.path.join(csrc, f) for f in FORWARD_SOURCES] + [os.path.join(ROOT, "include", "rr.h")]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:

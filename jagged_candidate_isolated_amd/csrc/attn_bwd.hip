@@ -26,6 +26,18 @@
 // key column per lane and accumulates dv^T = dO^T P and dk^T = q^T dS the same way.
 #include "mfma_tile.h"
 
+// Tuning knobs: k_bwd_dq's key tile per head dimension, and the smallest head dimension
+// whose k_bwd_dkdv reads V operands from LDS rather than registers.
+#ifndef RR_BWD_DQ_BN64
+#define RR_BWD_DQ_BN64 32
+#endif
+#ifndef RR_BWD_DQ_BN128
+#define RR_BWD_DQ_BN128 32
+#endif
+#ifndef RR_BWD_VLDS_MIN_D
+#define RR_BWD_VLDS_MIN_D 128
+#endif
+
 namespace rr {
 namespace {
 
@@ -394,7 +406,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const
 
 template <int D>
 __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
-  constexpr bool VLDS = D >= 128;   // the V operands of the item's 128 keys from LDS
+  constexpr bool VLDS = D >= RR_BWD_VLDS_MIN_D;   // the V operands of the item's 128 keys from LDS
   __shared__ __attribute__((aligned(16))) u16 q0[kQw * D], q1[kQw * D], d0[kQw * D], d1[kQw * D];
   __shared__ __attribute__((aligned(16))) u16 vb[VLDS ? kBwdRows * D : 8];
   __shared__ __attribute__((aligned(16))) float l0[64], l1[64];
@@ -415,7 +427,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
 
 template <int D>
 hipError_t go(const BwdArgs& g, int64_t grid, hipStream_t s) {
-  constexpr int BN = D == 128 ? 32 : 64;   // key tile of k_bwd_dq (register budget)
+  constexpr int BN = D == 128 ? RR_BWD_DQ_BN128 : RR_BWD_DQ_BN64;   // key tile of k_bwd_dq (register budget)
   hipError_t e = launch1(k_bwd_dq<D, BN>, grid, kBwdWaves * 64, s, g);
   if (e != hipSuccess) return e;
   return launch1(k_bwd_dkdv<D>, grid, kBwdWaves * 64, s, g);
