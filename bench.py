@@ -75,12 +75,12 @@ FORWARD_SOURCES = ("attn_mfma.hip", "mfma_tile.h", "rr_internal.h", "schedule.hi
 
 
 def source_hash() -> str:
-    """Digest of the forward attention step's sources (and the ABI header): traffic counters
-    taken on other sources are not reported."""
+    """Digest of the forward attention step's sources: traffic counters taken on other
+    sources are not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jagged_candidate_isolated_amd", "csrc")
-    files = [os.path.join(csrc, f) for f in FORWARD_SOURCES] + [os.path.join(ROOT, "include", "rr.h")]
+    files = [os.path.join(csrc, f) for f in FORWARD_SOURCES]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:

@@ -113,6 +113,11 @@ size_t rr_attn_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d);
  * valid       uint8 [T] device or NULL; attend_padded_history as in rr_segment_ids
  * scale       softmax scale; <= 0 selects 1/sqrt(d)
  * workspace   device scratch of at least rr_attn_workspace_bytes(B, T, H, d) bytes
+ *
+ * A small unpadded bf16 batch (valid == NULL, at most 256 users, a grid of at most 1024
+ * workgroups) is planned inside the attention kernel: one launch, and no plan is left in
+ * the workspace.  Larger or padded batches run rr_attn_plan + rr_attn_run.  Both give the
+ * same bits.
  */
 int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
                 const int32_t* cand_start, const uint8_t* valid, int attend_padded_history,

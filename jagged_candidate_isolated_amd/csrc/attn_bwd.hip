@@ -37,6 +37,9 @@
 #ifndef RR_BWD_VLDS_MIN_D
 #define RR_BWD_VLDS_MIN_D 128
 #endif
+#ifndef RR_BWD_DKDV_BQ64
+#define RR_BWD_DKDV_BQ64 32
+#endif
 
 namespace rr {
 namespace {
@@ -264,10 +267,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dq(BwdArgs g) {
 // --------------------------------------------------------------------------- dk, dv
 
 // KEY_IDX: the key list goes through idx; QRY_IDX: the query list does (an indexed plan)
-template <int D, bool KEY_IDX, bool QRY_IDX, bool VLDS>
+template <int D, int BQ, bool KEY_IDX, bool QRY_IDX, bool VLDS>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const UserMeta& um,
                                           const Stages& st, float* const (&ls)[2], u16* vblock) {
-  constexpr int NS = 2, BQ = kQw, kThreads = kBwdWaves * 64;
+  constexpr int NS = 2, QB = BQ / kQw, kThreads = kBwdWaves * 64;
+  static_assert(BQ % kQw == 0, "query tile");
   constexpr bool indexed = QRY_IDX;
   using Loader = KvLoader<D, BQ, kThreads, QRY_IDX>;     // query rows (Q and dO) of one tile
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
@@ -301,17 +305,20 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const
     vl.issue_v(kt, vblock);
   }
 
-  // query tiles of BQ rows: Q and dO rows, and the rows' lse and delta (lanes 0-31 and
-  // 32-63 of one 4-byte load per wave; every wave loads the same 256 bytes)
+  // query tiles of BQ rows: Q and dO rows, and the rows' lse and delta (per 32-row block,
+  // lanes 0-31 and 32-63 of one 4-byte load per wave; every wave loads the same bytes)
   const Loader ld(Qp, DOp, a.idx, rs, um.q_begin, n_q, tid);
   const int nqt = (n_q + BQ - 1) / BQ;
   auto issue = [&](int t, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     ld.issue(t, st.k[S], st.v[S]);
-    const int e = um.q_begin + min(t * BQ + ql, n_q - 1);
-    const int64_t r = indexed ? a.idx[e] : e;
-    const float* src = (half ? static_cast<const float*>(g.delta) : g.lse) + r * a.H + h;
-    lds_dma_global4(src, __builtin_amdgcn_readfirstlane(lds_address(ls[S])));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int e = um.q_begin + min(t * BQ + qb * kQw + ql, n_q - 1);
+      const int64_t r = indexed ? a.idx[e] : e;
+      const float* src = (half ? static_cast<const float*>(g.delta) : g.lse) + r * a.H + h;
+      lds_dma_global4(src, __builtin_amdgcn_readfirstlane(lds_address(ls[S] + 64 * qb)));
+    }
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
@@ -339,51 +346,62 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const
     const char* sd = reinterpret_cast<const char*>(st.v[CUR]);
     const LDS_AS float* sl = (const LDS_AS float*)ls[CUR];
     // S = Q K^T and dP = dO V^T (rows: queries of this tile, column: this lane's key)
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    f32x16 sacc[QB], pacc[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { sacc[qb] = f32x16{}; pacc[qb] = f32x16{}; }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sq + q_off[kk]),
-                                                     kf[kk], sacc, 0, 0, 0);
       bf16x8 vop;
       if constexpr (VLDS)
         vop = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(vblock) + q_off[kk] +
                                                wave * kQw * CH * 16);
       else
         vop = vf[kk];
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sd + q_off[kk]),
-                                                     vop, pacc, 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const uint32_t o = q_off[kk] + qb * kQw * CH * 16;
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sq + o), kf[kk],
+                                                           sacc[qb], 0, 0, 0);
+        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sd + o), vop,
+                                                           pacc[qb], 0, 0, 0);
+      }
     }
     if ((t + 1) * BQ > n_q) {   // query rows past the list: P = 0
-      const int lim = n_q - t * BQ - 4 * half;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 8 * (r >> 2) + (r & 3);
-        sacc[r] += __int_as_float(~((c - lim) >> 31) & static_cast<int>(0xff800000u));
+      for (int qb = 0; qb < QB; ++qb) {
+        const int lim = n_q - t * BQ - qb * kQw - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          sacc[qb][r] += __int_as_float(~((c - lim) >> 31) & static_cast<int>(0xff800000u));
+        }
       }
     }
     // P = exp(scale s - lse) and dS = P (dP - delta), per query row 8(r/4) + 4 half + r%4
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      typedef float f32x4 __attribute__((ext_vector_type(4)));
-      const f32x4 lv = *(const LDS_AS f32x4*)(sl + 8 * gq + 4 * half);
-      const f32x4 dv4 = *(const LDS_AS f32x4*)(sl + 32 + 8 * gq + 4 * half);
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * gq + u;
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -lv[u] * kLog2e));
-        sacc[r] = p;
-        pacc[r] = p * (pacc[r] - dv4[u]);
+      for (int gq = 0; gq < 4; ++gq) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 lv = *(const LDS_AS f32x4*)(sl + 64 * qb + 8 * gq + 4 * half);
+        const f32x4 dv4 = *(const LDS_AS f32x4*)(sl + 64 * qb + 32 + 8 * gq + 4 * half);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * gq + u;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], sl2, -lv[u] * kLog2e));
+          sacc[qb][r] = p;
+          pacc[qb][r] = p * (pacc[qb][r] - dv4[u]);
+        }
       }
-    }
     // dv^T += dO^T P and dk^T += Q^T dS (dO^T, Q^T read transposed, in P's row order)
 #pragma unroll
     for (int ks = 0; ks < BQ / 16; ++ks) {
-      const int s8 = ks * 8;
+      const int qb = ks >> 1, s8 = (ks & 1) * 8;
       bf16x8 pf, sf;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        pf[j] = static_cast<__bf16>(sacc[s8 + j]);
-        sf[j] = static_cast<__bf16>(pacc[s8 + j]);
+        pf[j] = static_cast<__bf16>(sacc[qb][s8 + j]);
+        sf[j] = static_cast<__bf16>(pacc[qb][s8 + j]);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -407,9 +425,10 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const
 template <int D>
 __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
   constexpr bool VLDS = D >= RR_BWD_VLDS_MIN_D;   // the V operands of the item's 128 keys from LDS
-  __shared__ __attribute__((aligned(16))) u16 q0[kQw * D], q1[kQw * D], d0[kQw * D], d1[kQw * D];
+  constexpr int BQ = D == 64 ? RR_BWD_DKDV_BQ64 : kQw;   // query rows per tile
+  __shared__ __attribute__((aligned(16))) u16 q0[BQ * D], q1[BQ * D], d0[BQ * D], d1[BQ * D];
   __shared__ __attribute__((aligned(16))) u16 vb[VLDS ? kBwdRows * D : 8];
-  __shared__ __attribute__((aligned(16))) float l0[64], l1[64];
+  __shared__ __attribute__((aligned(16))) float l0[2 * BQ], l1[2 * BQ];
   const Stages st{{q0, q1, q0, q1}, {d0, d1, d0, d1}};
   float* const ls[2] = {l0, l1};
   int2 it;
@@ -420,9 +439,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
   if (item_head(it) == kZeroHead) return;
   const int kt = item_tile(it) * subs + w % subs;
   if (kt * kBwdRows >= um.n_kv) return;   // no keys in this tile
-  if (!indexed) dkdv_item<D, false, false, VLDS>(g, item_head(it), kt, um, st, ls, vb);
-  else if (um.kv_direct) dkdv_item<D, false, true, VLDS>(g, item_head(it), kt, um, st, ls, vb);
-  else dkdv_item<D, true, true, VLDS>(g, item_head(it), kt, um, st, ls, vb);
+  if (!indexed) dkdv_item<D, BQ, false, false, VLDS>(g, item_head(it), kt, um, st, ls, vb);
+  else if (um.kv_direct) dkdv_item<D, BQ, false, true, VLDS>(g, item_head(it), kt, um, st, ls, vb);
+  else dkdv_item<D, BQ, true, true, VLDS>(g, item_head(it), kt, um, st, ls, vb);
 }
 
 template <int D>
