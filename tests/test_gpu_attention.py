@@ -273,3 +273,28 @@ def test_self_planned_equals_planned(cfg):
     assert np.array_equal(fused, planned)
     if cfg != 2:
         assert_close(fused, _oracle_full(fb), "bf16", f"self-planned {cfg}")
+
+
+@pytest.mark.parametrize("B", [1, 17, 100, 256])
+def test_self_planned_random_batches(B):
+    """In-kernel planning on random small batches (many users in one key-count bucket,
+    empty users, users with no history): bit-identical to plan + run."""
+    from _gpu import rr
+    rng = np.random.default_rng(B)
+    P = rng.integers(0, 4, B)
+    h = np.where(rng.random(B) < 0.5, 37, rng.integers(0, 200 if B <= 100 else 60, B)) * (rng.random(B) > 0.1)
+    c = rng.integers(0, 40, B) * (rng.random(B) > 0.1)
+    H = 2 if B <= 100 else 1
+    fb = W.make_full_batch(rng, f"selfplan{B}", prefix=P, hist=h, cand=c, H=H, d=64, seed=9100 + B)
+    # the library plans in-kernel for at most 256 users and a grid of at most 1024 workgroups
+    grid = -(-(H + 1) * (-(-fb.T // 128) + B) // 64) * 64
+    assert fb.T < 2048 * B and grid <= 1024, "the batch must take the in-kernel planning path"
+    dev = full_dev(fb)
+    fused = run_full(fb, dev)
+    ws = rr().rr_attn_plan(dev["offsets"], dev["cand_start"], fb.T, fb.H, fb.d, dev["q"].dtype)
+    out = rr().rr_attn_run(dev["q"], dev["k"], dev["v"], fb.B, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(fused, out.float().cpu().numpy().astype(np.float64))
+    rows, heads = sample_full_rows(fb, per_user=1, seed=B)
+    assert_close(fused[rows, heads], A.full_attention_rows(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, rows,
+                                                           heads), "bf16", f"self-planned B={B}")
