@@ -571,13 +571,11 @@ int rr_ranker_fwd(float* x, const rr_layer* layers, int32_t n_layers, int32_t n_
     const rr_layer& L = layers[l];
     RR_TRY(st(launch_rms_norm(x, L.norm_gain, h, T, D, kRmsEps, stream)));
     RR_TRY(st(launch_gemm_bt(h, L.w_qkv, T, 3 * D, D, qkv, D, nullptr, stream)));
-    RR_TRY(st(launch_rope_qk(q, k, q, k, offsets, cand_start, nullptr, B, T, H, d, RR_BF16, lb, stream)));
-    if (cache) {   // this layer's history keys (rotated) and values, compacted
-      RR_TRY(st(launch_split_rows(k, int64_t(D) * 2, offsets, cand_start, hoff, coff, B, T,
-                                  cache + (2 * l) * layer_elems, Th, nullptr, 0, stream)));
-      RR_TRY(st(launch_split_rows(v, int64_t(D) * 2, offsets, cand_start, hoff, coff, B, T,
-                                  cache + (2 * l + 1) * layer_elems, Th, nullptr, 0, stream)));
-    }
+    // the rotary pass also writes this layer's history keys (rotated) and values, compacted,
+    // into the cache
+    RR_TRY(st(launch_rope_qk_cache(q, k, q, k, offsets, cand_start, nullptr, B, T, H, d, RR_BF16, lb,
+                                   cache ? cache + (2 * l) * layer_elems : nullptr, v,
+                                   cache ? cache + (2 * l + 1) * layer_elems : nullptr, hoff, Th, stream)));
     RR_TRY(rr_attn_run(q, k, v, o, B, T, H, d, RR_BF16, 0.f, wa, wa_bytes, stream));
     RR_TRY(st(launch_gemm_bt(o, L.w_o, T, D, D, nullptr, 0, x, stream)));
   }

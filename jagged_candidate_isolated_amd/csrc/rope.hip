@@ -35,6 +35,13 @@ struct RopeArgs {
   int32_t H;
   int32_t d;
   double log2_base;
+  // optional: rows before their user's candidate start also go, k rotated, to the
+  // compact history blocks kc / vc (row hoff[b] + r - offsets[b] < Th); v is copied
+  void* kc;
+  const void* v;
+  void* vc;
+  const int32_t* hoff;
+  int32_t Th;
 };
 
 // The user owning row r: the last b in [0, B) with offsets[b] <= r (0 if none).
@@ -113,10 +120,12 @@ __device__ __forceinline__ void store2(__bf16* p, const float* y) {
   *reinterpret_cast<unsigned*>(p) = __builtin_bit_cast(unsigned, v);
 }
 
-// rotate NP pairs (2 NP elements at `first`) of every head of x into y
+// rotate NP pairs (2 NP elements at `first`) of every head of x into y (and into y2 at
+// `first2` when y2 is given)
 template <int NP, typename T>
 __device__ __forceinline__ void rotate_heads(const T* x, T* y, int64_t first, int H, int d,
-                                             const float* c, const float* s) {
+                                             const float* c, const float* s, T* y2 = nullptr,
+                                             int64_t first2 = 0) {
   constexpr int HU = 4;   // heads in flight
   for (int h0 = 0; h0 < H; h0 += HU) {
     float v[HU][2 * NP];
@@ -137,26 +146,62 @@ __device__ __forceinline__ void rotate_heads(const T* x, T* y, int64_t first, in
         }
         if constexpr (NP == 4) store8(y + first + static_cast<int64_t>(h0 + u) * d, w);
         else store2(y + first + static_cast<int64_t>(h0 + u) * d, w);
+        if (y2) {
+          if constexpr (NP == 4) store8(y2 + first2 + static_cast<int64_t>(h0 + u) * d, w);
+          else store2(y2 + first2 + static_cast<int64_t>(h0 + u) * d, w);
+        }
       }
   }
 }
 
-// NP = 4: one thread per 4 consecutive pairs (d % 8 == 0); NP = 1 otherwise
-template <typename T, int NP>
+// copy NP pairs of every head of row `first` of x to y at `first2`
+template <int NP, typename T>
+__device__ __forceinline__ void copy_heads(const T* x, T* y, int64_t first, int64_t first2, int H, int d) {
+  for (int h = 0; h < H; ++h) {
+    const int64_t o = static_cast<int64_t>(h) * d;
+    if constexpr (NP == 4 && sizeof(T) == 2) {
+      *reinterpret_cast<uint4*>(y + first2 + o) = *reinterpret_cast<const uint4*>(x + first + o);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2 * NP; ++j) y[first2 + o + j] = x[first + o + j];
+    }
+  }
+}
+
+// NP = 4: one thread per 4 consecutive pairs (d % 8 == 0); NP = 1 otherwise.  CACHE: also
+// fill the compact history blocks (a.kc, a.vc).
+template <typename T, int NP, bool CACHE>
 __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
   const int groups = a.d / (2 * NP);
   const int64_t n = static_cast<int64_t>(a.T) * groups;
   for (int64_t g = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; g < n;
        g += int64_t(gridDim.x) * blockDim.x) {
     const int r = static_cast<int>(g / groups), i0 = static_cast<int>(g % groups) * NP;
-    const int p = position_of(a, r);
+    const int b = user_of(a.offsets, a.B, r);
+    const int off = a.offsets[b];
+    const int p = (a.pos_base ? a.pos_base[b] : 0) + min(r - off, a.cand_start[b] - off);
     float c[NP], s[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j)
       rotary_sincos(p, exp2(-(2.0 * (i0 + j) / a.d) * a.log2_base), c[j], s[j]);
     const int64_t first = static_cast<int64_t>(r) * a.H * a.d + 2 * i0;
     if (a.q) rotate_heads<NP>(static_cast<const T*>(a.q), static_cast<T*>(a.qo), first, a.H, a.d, c, s);
-    if (a.k) rotate_heads<NP>(static_cast<const T*>(a.k), static_cast<T*>(a.ko), first, a.H, a.d, c, s);
+    if constexpr (CACHE) {
+      // a history row's place in the compact history blocks
+      int64_t hrow = -1;
+      if (r < a.cand_start[b]) {
+        hrow = static_cast<int64_t>(a.hoff[b]) + r - off;
+        if (hrow >= a.Th) hrow = -1;
+      }
+      const int64_t first2 = hrow * a.H * a.d + 2 * i0;
+      if (a.k)
+        rotate_heads<NP>(static_cast<const T*>(a.k), static_cast<T*>(a.ko), first, a.H, a.d, c, s,
+                         hrow >= 0 && a.kc ? static_cast<T*>(a.kc) : nullptr, first2);
+      if (a.vc && hrow >= 0)
+        copy_heads<NP>(static_cast<const T*>(a.v), static_cast<T*>(a.vc), first, first2, a.H, a.d);
+    } else if (a.k) {
+      rotate_heads<NP>(static_cast<const T*>(a.k), static_cast<T*>(a.ko), first, a.H, a.d, c, s);
+    }
   }
 }
 
@@ -190,17 +235,33 @@ hipError_t launch_rope_positions(const int32_t* offsets, const int32_t* cand_sta
 hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,
                           const int32_t* cand_start, const int32_t* pos_base, int B, int T, int H,
                           int d, int dtype, double log2_base, hipStream_t s) {
+  return launch_rope_qk_cache(q, k, qo, ko, offsets, cand_start, pos_base, B, T, H, d, dtype, log2_base, nullptr,
+                              nullptr, nullptr, nullptr, 0, s);
+}
+
+hipError_t launch_rope_qk_cache(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,
+                                const int32_t* cand_start, const int32_t* pos_base, int B, int T, int H, int d,
+                                int dtype, double log2_base, void* kc, const void* v, void* vc,
+                                const int32_t* hoff, int Th, hipStream_t s) {
   RopeArgs a = rope_args(offsets, cand_start, pos_base, B, T);
   a.q = q; a.k = k; a.qo = qo; a.ko = ko;
   a.H = H; a.d = d; a.log2_base = log2_base;
+  a.kc = kc; a.v = v; a.vc = vc; a.hoff = hoff; a.Th = Th;
+  const bool cache = (kc || vc) && hoff;
   if (d % 8 == 0) {
     const int64_t grid = grid_for(static_cast<int64_t>(T) * (d / 8));
-    return dtype == RR_BF16 ? launch1(k_rope_qk<__bf16, 4>, grid, 256, s, a)
-                            : launch1(k_rope_qk<float, 4>, grid, 256, s, a);
+    if (cache)
+      return dtype == RR_BF16 ? launch1(k_rope_qk<__bf16, 4, true>, grid, 256, s, a)
+                              : launch1(k_rope_qk<float, 4, true>, grid, 256, s, a);
+    return dtype == RR_BF16 ? launch1(k_rope_qk<__bf16, 4, false>, grid, 256, s, a)
+                            : launch1(k_rope_qk<float, 4, false>, grid, 256, s, a);
   }
   const int64_t grid = grid_for(static_cast<int64_t>(T) * (d / 2));
-  return dtype == RR_BF16 ? launch1(k_rope_qk<__bf16, 1>, grid, 256, s, a)
-                          : launch1(k_rope_qk<float, 1>, grid, 256, s, a);
+  if (cache)
+    return dtype == RR_BF16 ? launch1(k_rope_qk<__bf16, 1, true>, grid, 256, s, a)
+                            : launch1(k_rope_qk<float, 1, true>, grid, 256, s, a);
+  return dtype == RR_BF16 ? launch1(k_rope_qk<__bf16, 1, false>, grid, 256, s, a)
+                          : launch1(k_rope_qk<float, 1, false>, grid, 256, s, a);
 }
 
 }  // namespace rr

@@ -318,6 +318,12 @@ hipError_t launch_rope_positions(const int32_t* offsets, const int32_t* cand_sta
 hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,
                           const int32_t* cand_start, const int32_t* pos_base, int B, int T, int H,
                           int d, int dtype, double log2_base, hipStream_t s);
+// launch_rope_qk that also writes the rows before each user's candidate start into the
+// compact history blocks kc (rotated k) and vc (a copy of v), row hoff[b] + r - offsets[b]
+hipError_t launch_rope_qk_cache(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,
+                                const int32_t* cand_start, const int32_t* pos_base, int B, int T, int H, int d,
+                                int dtype, double log2_base, void* kc, const void* v, void* vc,
+                                const int32_t* hoff, int Th, hipStream_t s);
 
 // Zero the output rows of a padding tile: rows idx[q_begin + n_q + qt*bm ...], every head
 // (and set their log-sum-exp to -inf when the forward writes it).
