@@ -69,23 +69,11 @@ def parse_args():
     return p.parse_args()
 
 
-# the sources the forward attention step is built from: its kernel, the shared tile
-# helpers, the plan (work list and padded-row compaction) and the launch logic
-FORWARD_SOURCES = ("attn_mfma.hip", "mfma_tile.h", "rr_internal.h", "schedule.hip", "segments.hip", "api.hip")
-
-
 def source_hash() -> str:
-    """Digest of the forward attention step's sources: traffic counters taken on other
-    sources are not reported."""
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "jagged_candidate_isolated_amd", "csrc")
-    files = [os.path.join(csrc, f) for f in FORWARD_SOURCES]
-    for f in files:
-        h.update(os.path.relpath(f, ROOT).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    """Digest of the forward attention kernels' machine code in the loaded library
+    (rr_forward_fingerprint): traffic counters taken on other kernels are not reported."""
+    from jagged_candidate_isolated_amd import rr
+    return rr.rr_forward_fingerprint()
 
 
 def measured_traffic(workload: str):

@@ -69,6 +69,10 @@ const char* rr_status_string(int status);
 /* Library ABI version (increments when a signature changes). */
 int rr_abi_version(void);
 
+/* Digest of the forward attention kernels' gfx950 machine code in this build: equal
+ * digests mean equal forward kernels, so a profile taken on one build applies to another. */
+const char* rr_forward_fingerprint(void);
+
 /*
  * rr_segment_ids -- per-row segment IDs.
  * Candidate isolation attention mask page, section "段 ID：掩码的表达方式":

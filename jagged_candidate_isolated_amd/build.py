@@ -50,6 +50,31 @@ def _run(cmd, verbose):
         sys.stderr.write("\n".join(noise) + "\n")
 
 
+# The forward attention step's device code (its kernel and the planning kernel): the
+# digest of their gfx950 assembly is built into the library (rr_forward_fingerprint), so
+# measurements taken on one build can be matched to another with the same machine code.
+FINGERPRINT_SOURCES = ("attn_mfma.hip", "schedule.hip")
+
+
+def _fingerprint_source(common, verbose) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in FINGERPRINT_SOURCES:
+        src = os.path.join(CSRC, name)
+        asm = os.path.join(BUILD_DIR, name + ".s")
+        _run(common + FILE_FLAGS.get(name, []) + ["--cuda-device-only", "-S", src, "-o", asm], verbose)
+        with open(asm, encoding="utf-8", errors="replace") as f:
+            for line in f:
+                # compilation-unit ids and file/tool stamps differ between otherwise equal builds
+                if "__hip_cuid" in line or line.lstrip().startswith((".file", ".ident")):
+                    continue
+                h.update(line.encode())
+    out = os.path.join(BUILD_DIR, "rr_fingerprint.cpp")
+    with open(out, "w", encoding="utf-8") as f:
+        f.write('extern "C" const char* rr_forward_fingerprint(void) { return "%s"; }\n' % h.hexdigest()[:16])
+    return out
+
+
 def build(verbose: bool = False) -> str:
     from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -59,6 +84,9 @@ def build(verbose: bool = False) -> str:
     for src in sources():
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         jobs.append((common + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj], obj))
+    fp = _fingerprint_source(common, verbose)
+    fp_obj = os.path.join(BUILD_DIR, "rr_fingerprint.o")
+    jobs.append(([hipcc(), "-O2", "-fPIC", "-c", "-x", "c++", fp, "-o", fp_obj], fp_obj))
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
     out_tmp = LIB + ".tmp"

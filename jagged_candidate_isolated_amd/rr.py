@@ -22,6 +22,7 @@ _I = ctypes.c_int32
 _SIGS = {
     "rr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rr_abi_version": (ctypes.c_int, []),
+    "rr_forward_fingerprint": (ctypes.c_char_p, []),
     "rr_segment_ids": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, _I, _I, _P, _P]),
     "rr_bounds": (ctypes.c_int, [_P, _P, _I, _I, _P, _P]),
     "rr_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -608,3 +609,8 @@ def rr_user_token_attn(q, k, v, key_offsets, query_offsets, scale=None, out=None
 
 def rr_ranker_cached_workspace_bytes(B: int, Th: int, Tc: int, H: int, d: int) -> int:
     return int(_lib.rr_ranker_cached_workspace_bytes(B, Th, Tc, H, d))
+
+
+def rr_forward_fingerprint() -> str:
+    """Digest of the forward attention kernels' machine code in the loaded library."""
+    return _lib.rr_forward_fingerprint().decode()
