@@ -298,3 +298,40 @@ def test_self_planned_random_batches(B):
     rows, heads = sample_full_rows(fb, per_user=1, seed=B)
     assert_close(fused[rows, heads], A.full_attention_rows(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, rows,
                                                            heads), "bf16", f"self-planned B={B}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_maximum_heads(d):
+    """H = 1023, the largest head count a work item can carry: full-sequence and
+    candidate-only attention on a small batch, every head of sampled rows against the
+    oracle, and the head past the limit rejected."""
+    from _gpu import rr
+    rng = np.random.default_rng(d)
+    H = 1023
+    fb = W.make_full_batch(rng, "max-heads", prefix=[1, 0], hist=[40, 3], cand=[5, 2], H=H, d=d,
+                           seed=9300 + d)
+    got = run_full(fb)
+    rows = np.array([0, 20, 40, 41, 45, 46, 49, 50], dtype=np.int64)
+    rows = rows[rows < fb.T]
+    for h in (0, 511, 1022):
+        ref = A.full_attention_rows(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, rows,
+                                    np.full(len(rows), h))
+        assert_close(got[rows, h], ref, "bf16", f"H=1023 head {h}")
+    cb = W.split_to_cand_only(fb)
+    co = run_cand_only(cb)
+    assert np.array_equal(co, got[cb.meta["cand_rows"]])
+    q = torch.zeros((4, H + 1, d), dtype=torch.bfloat16, device="cuda")
+    off = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    with pytest.raises(rr().RRError):
+        rr().rr_attn_fwd(q, q, q, off, torch.tensor([2], dtype=torch.int32, device="cuda"))
+
+
+def test_one_long_user():
+    """A single user of 60,000 rows (one long key chain per query tile, offsets far past
+    16 bits): sampled rows against the oracle, and candidates read only history + self."""
+    fb = W.make_full_batch(np.random.default_rng(3), "long-user", prefix=[4], hist=[59000], cand=[996],
+                           H=2, d=128, seed=9400)
+    got = run_full(fb)
+    rows, heads = sample_full_rows(fb, per_user=24, seed=4)
+    assert_close(got[rows, heads], A.full_attention_rows(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, rows,
+                                                         heads), "bf16", "one long user")
