@@ -50,10 +50,10 @@ def _run(cmd, verbose):
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-# The forward attention step's device code (its kernel and the planning kernel): the
-# digest of their gfx950 assembly is built into the library (rr_forward_fingerprint), so
-# measurements taken on one build can be matched to another with the same machine code.
-FINGERPRINT_SOURCES = ("attn_mfma.hip", "schedule.hip")
+# The forward attention kernels' device code: the digest of their gfx950 assembly is built
+# into the library (rr_forward_fingerprint), so measurements taken on one build can be
+# matched to another with the same machine code.
+FINGERPRINT_SOURCES = ("attn_mfma.hip",)
 
 
 def _fingerprint_source(common, verbose) -> str:

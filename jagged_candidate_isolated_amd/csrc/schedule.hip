@@ -28,6 +28,7 @@ struct WorklistParams {
   int mode;              // 0: full sequence (offs_a = offsets, offs_b = cand_start)
                          // 1: candidate-only (offs_a = hist_offsets, offs_b = cand_offsets)
                          // 2: as 1 with no self-term (user-token rows: offs_b = their offsets)
+                         // 3: as 1, items over key tiles (the key-major backward kernel)
   const int32_t* offs_a;
   const int32_t* offs_b;
   int meta_ready;        // meta[] already written by the compaction prologue
@@ -43,9 +44,11 @@ struct WorklistParams {
   PlanHeader* header;
 };
 
-// Items of one user: H per query tile, plus one per tile of padding rows to zero.
-__device__ __forceinline__ int user_items(const UserMeta& m, int H, int bm, int& nqt, int& nzt) {
-  nqt = (max(m.n_q, 0) + bm - 1) / bm;
+// Items of one user: H per query tile (per key tile in a key-major plan), plus one per
+// tile of padding rows to zero.
+__device__ __forceinline__ int user_items(const UserMeta& m, int H, int bm, int& nqt, int& nzt,
+                                          bool key_major) {
+  nqt = (max(key_major ? m.n_kv : m.n_q, 0) + bm - 1) / bm;
   nzt = (max(m.n_pad, 0) + bm - 1) / bm;
   return H * nqt + nzt;
 }
@@ -117,10 +120,10 @@ __global__ __launch_bounds__(kThreads) void k_worklist(WorklistParams p) {
     if (!p.meta_ready) p.meta[b] = m;
     if (in_lds) {
       int nqt, nzt;
-      user_items(m, p.H, p.bm, nqt, nzt);
+      user_items(m, p.H, p.bm, nqt, nzt, p.mode == 3);
       s_nqt[b] = nqt;
       s_nzt[b] = nzt;
-      const int k = cost_bucket(m.n_kv);
+      const int k = cost_bucket(p.mode == 3 ? m.n_q : m.n_kv);   // the length each item loops over
       s_bkt[b] = static_cast<unsigned char>(k);
       atomicAdd(&s_hist[k], 1);
     }
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_worklist(WorklistParams p) {
         cnt = p.H * s_nqt[b] + s_nzt[b];
       } else {
         int nqt, nzt;
-        cnt = user_items(p.meta[r], p.H, p.bm, nqt, nzt);
+        cnt = user_items(p.meta[r], p.H, p.bm, nqt, nzt, p.mode == 3);
       }
     }
     const int incl = block_inclusive_scan(cnt, s_wave);
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_worklist(WorklistParams p) {
       nzt = s_nzt[b];
     } else {
       b = r;
-      user_items(p.meta[b], p.H, p.bm, nqt, nzt);
+      user_items(p.meta[b], p.H, p.bm, nqt, nzt, p.mode == 3);
     }
     const int n_attn = p.H * nqt;
     int local = i - s0;
