@@ -16,7 +16,8 @@ What it computes (Candidate isolation attention mask page, sections
   5. right-anchored rotary positions and the rotary encoding of q and k (section
      "位置编码：候选共用一个位置"; ``rotary.py``);
   6. the gradients of the attention w.r.t. q, k, v and each row's log-sum-exp
-     (``backward.py``), from the forward's definition and the softmax derivative;
+     (``backward.py``), from the forward's definition and the softmax derivative, for
+     full-sequence and candidate-only layers;
   7. the ranker's layer stack (``ranker.py``): full layers, the split into frozen
      history and candidates, candidate-only layers, and the cached request that reuses
      the history's keys and values (section "只更新候选的末尾层"), each layer read as a
@@ -41,7 +42,10 @@ from .attention import (  # noqa: F401
 from .rotary import (  # noqa: F401
     right_anchored_positions, rotary_angles, rope, full_attention_rope, cand_only_attention_rope,
 )
-from .backward import full_attention_backward, attention_lse, gradient_error_scale  # noqa: F401
+from .backward import (  # noqa: F401
+    full_attention_backward, attention_lse, gradient_error_scale, cand_only_attention_backward,
+    cand_only_gradient_error_scale,
+)
 from .ranker import (  # noqa: F401
     Layer, rms_norm, block_full, block_cand_only, block_user_token_layer, history_kv,
     split_history_and_candidates,

@@ -12,6 +12,9 @@ definition -- per user and head, P = softmax(scale * q k^T masked by the explici
     dq = scale * dS k,   dk = scale * dS^T q
 
 Rows that admit no key (segment 0) have P = 0: they get no gradient and give none.
+A candidate-only layer's gradients are those of its fallback (the full layer over
+[frozen history | candidates], keeping the candidate rows): the same formulas with a
+zero output gradient on the history rows.
 ``attention_lse`` gives each row's log-sum-exp of its admitted scaled scores (natural
 log), the statistic a backward pass reuses from the forward; -inf for such rows.
 
@@ -135,3 +138,52 @@ def gradient_error_scale(q, k, v, do, offsets, cand_start, valid=None, attend_pa
             eq[lo:hi, h], ek[lo:hi, h], ev[lo:hi, h] = _user_head_error_scale(
                 q[lo:hi, h], k[lo:hi, h], v[lo:hi, h], do[lo:hi, h], mask, sc)
     return eq, ek, ev
+
+
+def _cand_only_as_full(q_cand, k_hist, v_hist, k_cand, v_cand, do, hist_offsets, cand_offsets):
+    """The page's fallback layout of a candidate-only layer: per user [frozen history |
+    candidates] as one full-sequence user.  History rows are queries of the fallback too,
+    but the layer keeps only the candidate rows, so their output gradient is 0 (and their q
+    never matters).  Returns the full-layout arrays and the row maps."""
+    hoff = np.asarray(hist_offsets, np.int64)
+    coff = np.asarray(cand_offsets, np.int64)
+    B = len(coff) - 1
+    H, d = np.shape(q_cand)[1:]
+    hist_rows, cand_rows, offsets, cand_start = [], [], [0], []
+    for b in range(B):
+        base = offsets[-1]
+        nh, nc = int(hoff[b + 1] - hoff[b]), int(coff[b + 1] - coff[b])
+        hist_rows.append(np.arange(base, base + nh))
+        cand_rows.append(np.arange(base + nh, base + nh + nc))
+        cand_start.append(base + nh)
+        offsets.append(base + nh + nc)
+    T = offsets[-1]
+    hr = np.concatenate(hist_rows + [np.zeros(0, np.int64)]).astype(np.int64)
+    cr = np.concatenate(cand_rows + [np.zeros(0, np.int64)]).astype(np.int64)
+    q, k, v, g = (np.zeros((T, H, d)) for _ in range(4))
+    q[cr] = q_cand; k[hr] = k_hist; k[cr] = k_cand
+    v[hr] = v_hist; v[cr] = v_cand; g[cr] = do
+    return q, k, v, g, np.asarray(offsets, np.int64), np.asarray(cand_start, np.int64), hr, cr
+
+
+def cand_only_attention_backward(q_cand, k_hist, v_hist, k_cand, v_cand, do, hist_offsets, cand_offsets,
+                                 scale=None):
+    """Gradients of a candidate-only layer (Candidate isolation attention mask page, section
+    "只更新候选的末尾层") w.r.t. its five inputs for the candidates' output gradient ``do``:
+    (dq_cand, dk_hist, dv_hist, dk_cand, dv_cand), float64.  The layer is its fallback -- the
+    full layer over [frozen history | candidates] keeping the candidate rows -- so these are
+    that layer's gradients with a zero output gradient on the history rows."""
+    q, k, v, g, off, cs, hr, cr = _cand_only_as_full(q_cand, k_hist, v_hist, k_cand, v_cand, do,
+                                                     hist_offsets, cand_offsets)
+    dq, dk, dv = full_attention_backward(q, k, v, g, off, cs, scale=scale)
+    return dq[cr], dk[hr], dv[hr], dk[cr], dv[cr]
+
+
+def cand_only_gradient_error_scale(q_cand, k_hist, v_hist, k_cand, v_cand, do, hist_offsets, cand_offsets,
+                                   scale=None):
+    """``gradient_error_scale`` of the candidate-only layer, per gradient in the order of
+    ``cand_only_attention_backward``."""
+    q, k, v, g, off, cs, hr, cr = _cand_only_as_full(q_cand, k_hist, v_hist, k_cand, v_cand, do,
+                                                     hist_offsets, cand_offsets)
+    eq, ek, ev = gradient_error_scale(q, k, v, g, off, cs, scale=scale)
+    return eq[cr], ek[hr], ev[hr], ek[cr], ev[cr]

@@ -209,5 +209,49 @@ def pin_error_scale():
             assert np.all(np.abs(gr - g) <= 1.02 * u * (e + np.abs(g)) + 1e-300)
 
 
+def pin_cand_only_finite_differences():
+    """The candidate-only layer's gradients against central differences of the candidate-only
+    forward oracle (its own code path, not the fallback layout), every input element."""
+    from workloads import make_cand_only_batch
+    rng = rng_for(96)
+    cb = make_cand_only_batch(rng, "co-fd", hist=[3, 0, 2], cand=[2, 2, 1], H=1, d=3, dtype="f32", scaled=False)
+    do = rng.standard_normal(cb.q_cand.shape)
+    ins = [np.asarray(x, np.float64).copy() for x in (cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand)]
+    got = G.cand_only_attention_backward(*ins, do, cb.hist_offsets, cb.cand_offsets)
+
+    def loss(args):
+        return float(np.sum(A.cand_only_attention(*args, cb.hist_offsets, cb.cand_offsets) * do))
+    eps = 1e-6
+    for i, x in enumerate(ins):
+        num = np.zeros_like(x)
+        for j in np.ndindex(x.shape):
+            xp = [a.copy() for a in ins]; xm = [a.copy() for a in ins]
+            xp[i][j] += eps; xm[i][j] -= eps
+            num[j] = (loss(xp) - loss(xm)) / (2 * eps)
+        assert np.max(np.abs(num - got[i])) <= 1e-6, i
+
+
+def pin_cand_only_dq_independent_of_history_gradient():
+    """A candidate's dq and its own key's and value's gradients are those of the full layer's
+    candidate rows whatever output gradient the history rows carry there."""
+    from workloads import split_to_cand_only
+    rng = rng_for(97)
+    fb = make_full_batch(rng, "co-full", prefix=[1, 0], hist=[3, 2], cand=[2, 3], H=2, d=4, dtype="f32",
+                         scaled=False)
+    do = rng.standard_normal(fb.q.shape)
+    full = _grads(fb, do)
+    cb = split_to_cand_only(fb)
+    cr, hr = cb.meta["cand_rows"], cb.meta["hist_rows"]
+    got = G.cand_only_attention_backward(cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand, do[cr],
+                                         cb.hist_offsets, cb.cand_offsets)
+    assert np.max(np.abs(got[0] - full[0][cr])) <= 1e-12
+    assert np.max(np.abs(got[3] - full[1][cr])) <= 1e-12 and np.max(np.abs(got[4] - full[2][cr])) <= 1e-12
+    # the history keys differ by exactly the history queries' part: zero it in the full layer
+    do0 = do.copy(); do0[hr] = 0.0
+    full0 = _grads(fb, do0)
+    assert np.max(np.abs(got[1] - full0[1][hr])) <= 1e-12 and np.max(np.abs(got[2] - full0[2][hr])) <= 1e-12
+
+
 BWD_PINS = [pin_finite_differences, pin_torch_autograd, pin_lse, pin_closed_forms,
-            pin_isolation_of_gradients, pin_error_scale]
+            pin_isolation_of_gradients, pin_error_scale, pin_cand_only_finite_differences,
+            pin_cand_only_dq_independent_of_history_gradient]
