@@ -226,6 +226,34 @@ int rr_cand_only_run(const void* q_cand, const void* k_hist, const void* v_hist,
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Candidate-only layers: forward with log-sum-exp and backward (Candidate isolation
+ * attention mask page, section "只更新候选的末尾层"; gradients as for rr_attn_bwd, of the
+ * layer's fallback: the full layer over [frozen history | candidates] keeping the
+ * candidate rows, i.e. with no output gradient on the history rows).
+ *
+ * rr_cand_only_run_lse: rr_cand_only_run that also writes lse float [Tc][H], each
+ * candidate row's natural-log sum of exp(scale q.k) over the keys it reads.
+ *
+ * rr_cand_only_bwd_run: with the plan rr_cand_only_plan made in a workspace of
+ * rr_cand_only_bwd_workspace_bytes (the same workspace rr_cand_only_run_lse ran with),
+ * writes dq_cand [Tc][H][d], dk_hist, dv_hist [Th][H][d] (0 for the keys of users without
+ * candidates) and dk_cand, dv_cand [Tc][H][d] (a candidate's own key and value, read by it
+ * alone).  It builds a second plan whose items are key tiles of the frozen history.  bf16,
+ * d in {64, 128}; no atomics, so repeated calls give the same bits.  Outputs must not alias
+ * inputs.
+ */
+int rr_cand_only_run_lse(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                         const void* v_cand, void* o_cand, float* lse, int32_t B, int32_t Th, int32_t Tc, int32_t H,
+                         int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+size_t rr_cand_only_bwd_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d);
+int rr_cand_only_bwd_run(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                         const void* v_cand, const void* o_cand, const void* dout, const float* lse, void* dq_cand,
+                         void* dk_hist, void* dv_hist, void* dk_cand, void* dv_cand, const int32_t* hist_offsets,
+                         const int32_t* cand_offsets, int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d,
+                         int dtype, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * rr_rope_positions -- right-anchored positions of every row.
  * Candidate isolation attention mask page, section "位置编码：候选共用一个位置": the
  * newest history row sits at history_end - 1 whatever the history length, and every

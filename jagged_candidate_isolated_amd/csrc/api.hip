@@ -147,6 +147,34 @@ bool bwd_supported(int dtype, int d) { return dtype == RR_BF16 && (d == 64 || d 
 
 size_t bwd_delta_offset(int32_t B, int32_t T, int32_t H) { return align256(ws_layout(B, T, T, H).total); }
 
+// Candidate-only backward workspace: the forward's plan, the key-major plan, rowsum(dO * o).
+struct CandBwdWs {
+  size_t key_plan, delta, total;
+};
+CandBwdWs cand_bwd_layout(int32_t B, int32_t Th, int32_t Tc, int32_t H) {
+  CandBwdWs w{};
+  w.key_plan = align256(ws_layout(B, 0, Tc, H).total);
+  w.delta = w.key_plan + align256(ws_layout(B, 0, Th, H).total);
+  w.total = w.delta + align256(sizeof(float) * size_t(Tc) * size_t(H));
+  return w;
+}
+
+AttnArgs cand_args(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                   const void* v_cand, void* o_cand, int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d,
+                   float scale, const void* plan_ws, int mode) {
+  const Ws p = carve_all(const_cast<void*>(plan_ws), ws_layout(B, 0, mode == 3 ? Th : Tc, H));
+  AttnArgs a{};
+  a.q = q_cand;
+  a.k = Th > 0 ? k_hist : k_cand;   // with no frozen rows the key list is empty for every user
+  a.v = Th > 0 ? v_hist : v_cand;
+  a.k_self = k_cand; a.v_self = v_cand; a.o = o_cand;
+  a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
+  a.B = B; a.H = H; a.mode = mode; a.rows = Tc;
+  a.scale_log2 = softmax_scale_log2(scale, d);
+  return a;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -202,8 +230,8 @@ int rr_attn_bwd_run(const void* q, const void* k, const void* v, const void* o, 
   float* delta = carve<float>(workspace, bwd_delta_offset(B, T, H));
   const float sc = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf(static_cast<float>(d));
   const int bm = tile_rows(dtype, d, B, T);   // the plan rr_attn_plan made for these sizes
-  return status_of(launch_attn_bwd(a, dout, lse, dq, dk, dv, delta, sc, d, bm, attn_grid(B, T, H, bm),
-                                   stream));
+  const int64_t grid = attn_grid(B, T, H, bm);
+  return status_of(launch_attn_bwd(a, bm, grid, a, bm, grid, dout, lse, dq, dk, dv, dk, dv, delta, sc, d, stream));
 }
 
 int rr_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -312,6 +340,68 @@ int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_
 
 size_t rr_user_token_attn_workspace_bytes(int32_t B, int32_t Tk, int32_t Tq, int32_t H, int32_t d) {
   return rr_cand_only_workspace_bytes(B, Tk, Tq, H, d);
+}
+
+int rr_cand_only_run_lse(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                         const void* v_cand, void* o_cand, float* lse, int32_t B, int32_t Th, int32_t Tc, int32_t H,
+                         int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const int st = check_sizes(B, Th, Tc, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (B == 0 || Tc == 0 || H == 0) return RR_OK;
+  if (!q_cand || !k_cand || !v_cand || !o_cand) return RR_EINVAL;
+  if (Th > 0 && (!k_hist || !v_hist)) return RR_EINVAL;
+  if (!workspace || workspace_bytes < ws_layout(B, 0, Tc, H).total) return RR_EWORKSPACE;
+  AttnArgs a = cand_args(q_cand, k_hist, v_hist, k_cand, v_cand, o_cand, B, Th, Tc, H, d, scale, workspace, 1);
+  a.lse = lse;
+  return run_attention(a, dtype, d, tile_rows(dtype, d, B, Tc), Tc, stream);
+}
+
+size_t rr_cand_only_bwd_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d) {
+  if (check_sizes(B, Th, Tc, H, d, RR_BF16) != RR_OK || check_sizes(B, Tc, Th, H, d, RR_BF16) != RR_OK ||
+      !bwd_supported(RR_BF16, d))
+    return 0;
+  return cand_bwd_layout(B, Th, Tc, H).total;
+}
+
+int rr_cand_only_bwd_run(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                         const void* v_cand, const void* o_cand, const void* dout, const float* lse, void* dq_cand,
+                         void* dk_hist, void* dv_hist, void* dk_cand, void* dv_cand, const int32_t* hist_offsets,
+                         const int32_t* cand_offsets, int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d,
+                         int dtype, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_sizes(B, Th, Tc, H, d, dtype);
+  if (st == RR_OK) st = check_sizes(B, Tc, Th, H, d, dtype);   // the key-major plan's item bound
+  if (st != RR_OK) return st;
+  if (!bwd_supported(dtype, d)) return RR_EUNSUPPORTED;
+  if (B == 0 || H == 0 || (Th == 0 && Tc == 0)) return RR_OK;
+  if (!hist_offsets || !cand_offsets) return RR_EINVAL;
+  if (Tc > 0 && (!q_cand || !k_cand || !v_cand || !o_cand || !dout || !lse || !dq_cand || !dk_cand || !dv_cand))
+    return RR_EINVAL;
+  if (Th > 0 && (!k_hist || !v_hist || !dk_hist || !dv_hist)) return RR_EINVAL;
+  if (!workspace || workspace_bytes < rr_cand_only_bwd_workspace_bytes(B, Th, Tc, H, d)) return RR_EWORKSPACE;
+  const CandBwdWs w = cand_bwd_layout(B, Th, Tc, H);
+  void* key_ws = carve<char>(workspace, w.key_plan);
+  float* delta = carve<float>(workspace, w.delta);
+  // the key-major plan: items over each user's frozen history keys, 128 per tile
+  const Ws kp = carve_all(key_ws, ws_layout(B, 0, Th, H));
+  const int64_t grid_k = Th > 0 ? attn_grid(B, Th, H, kBmMfmaNarrow) : 0;
+  if (grid_k > 0) {
+    const hipError_t e = launch_worklist(3, hist_offsets, cand_offsets, 0, B, H, kBmMfmaNarrow, Tc, Th,
+                                         static_cast<int>(grid_k), kp.meta, kp.start, kp.items, kp.header, stream);
+    if (e != hipSuccess) return status_of(e);
+  }
+  const void* q = q_cand ? q_cand : k_hist;   // any rows in bounds: Tc == 0 launches no query-major work
+  const void* kc = k_cand ? k_cand : k_hist;
+  const void* vc = v_cand ? v_cand : v_hist;
+  const AttnArgs aq = cand_args(q, k_hist, v_hist, kc, vc, const_cast<void*>(o_cand), B, Th, Tc, H, d, scale,
+                                workspace, 1);
+  const AttnArgs ak = cand_args(q, k_hist, v_hist, kc, vc, const_cast<void*>(o_cand), B, Th, Tc, H, d, scale,
+                                key_ws, 3);
+  const float sc = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf(static_cast<float>(d));
+  const int bm_q = tile_rows(dtype, d, B, Tc);   // the plan rr_cand_only_plan made for these sizes
+  const int64_t grid_q = Tc > 0 ? attn_grid(B, Tc, H, bm_q) : 0;
+  return status_of(launch_attn_bwd(aq, bm_q, grid_q, ak, kBmMfmaNarrow, grid_k, dout, lse, dq_cand, dk_hist,
+                                   dv_hist, dk_cand, dv_cand, delta, sc, d, stream));
 }
 
 int rr_user_token_attn_plan(const int32_t* key_offsets, const int32_t* query_offsets, int32_t B, int32_t Tk,

@@ -14,7 +14,10 @@
 //   * a candidate's own key and value are read by that candidate alone, so their
 //     gradients come straight out of k_bwd_dq's self-term.
 // Every output row is written by exactly one workgroup (no atomics), so the result
-// is deterministic.  Both kernels take the forward's plan as it is (tiles of 128 or 256
+// is deterministic.  A candidate-only layer (Candidate isolation attention mask page,
+// section "只更新候选的末尾层") runs the same two kernels: the query-major one over its
+// candidates (own key and value gradients from the self-term), the key-major one over
+// the frozen history keys with a plan whose items are key tiles.  Both kernels take the forward's plan as it is (tiles of 128 or 256
 // query rows) and give each 128-row sub-tile of an item its own workgroup: query rows
 // in the query-major kernel; in the key-major kernel item (user, head, t) stands for
 // key tile t of the same height, which always exists because a user's keys are a
@@ -57,6 +60,8 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;          // [rows][H] rowsum(dO * O): written by k_bwd_dq, read by k_bwd_dkdv
+  void* dk_self;         // a candidate's own key and value gradients (dk, dv in full mode;
+  void* dv_self;         // the candidate tensors' gradients in a candidate-only layer)
   float scale;
   int bm;                // the plan's tile height (a multiple of kBwdRows)
 };
@@ -226,8 +231,8 @@ __device__ __forceinline__ void dq_item(const BwdArgs& g, int h, int qt, const U
         dqacc[db][4 * gg + 3] = fmaf(ds, bf16_hi(kw.y), dqacc[db][4 * gg + 3]);
       }
     if (qvalid) {
-      u16* dkp = static_cast<u16*>(g.dk) + h * D + rbase;
-      u16* dvp = static_cast<u16*>(g.dv) + h * D + rbase;
+      u16* dkp = static_cast<u16*>(g.dk_self) + h * D + rbase;
+      u16* dvp = static_cast<u16*>(g.dv_self) + h * D + rbase;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         store8(dkp + 16 * kk + 8 * half, qf[kk], g.scale * ds);   // dk_c = scale ds q_c
@@ -322,7 +327,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  issue(0, C0{});
+  if (nqt > 0) issue(0, C0{});   // a candidate-only user may have keys but no queries
 
   uint32_t q_off[KK];
 #pragma unroll
@@ -445,27 +450,31 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
 }
 
 template <int D>
-hipError_t go(const BwdArgs& g, int64_t grid, hipStream_t s) {
+hipError_t go(const BwdArgs& gq, int64_t grid_q, const BwdArgs& gk, int64_t grid_k, hipStream_t s) {
   constexpr int BN = D == 128 ? RR_BWD_DQ_BN128 : RR_BWD_DQ_BN64;   // key tile of k_bwd_dq (register budget)
-  hipError_t e = launch1(k_bwd_dq<D, BN>, grid, kBwdWaves * 64, s, g);
+  hipError_t e = launch1(k_bwd_dq<D, BN>, grid_q, kBwdWaves * 64, s, gq);
   if (e != hipSuccess) return e;
-  return launch1(k_bwd_dkdv<D>, grid, kBwdWaves * 64, s, g);
+  return launch1(k_bwd_dkdv<D>, grid_k, kBwdWaves * 64, s, gk);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dk,
-                           void* dv, float* delta, float scale, int d, int bm, int64_t grid,
-                           hipStream_t s) {
-  if (bm % kBwdRows != 0) return hipErrorInvalidValue;
-  grid *= bm / kBwdRows;   // one workgroup per 128-row sub-tile of every item
-  BwdArgs g{};
-  g.bm = bm;
-  g.a = a;
-  g.dout = dout; g.lse = lse; g.dq = dq; g.dk = dk; g.dv = dv; g.delta = delta; g.scale = scale;
+hipError_t launch_attn_bwd(const AttnArgs& aq, int bm_q, int64_t grid_q, const AttnArgs& ak, int bm_k,
+                           int64_t grid_k, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* dk_self, void* dv_self, float* delta, float scale, int d, hipStream_t s) {
+  if (bm_q % kBwdRows != 0 || bm_k % kBwdRows != 0) return hipErrorInvalidValue;
+  BwdArgs gq{};
+  gq.dout = dout; gq.lse = lse; gq.dq = dq; gq.dk = dk; gq.dv = dv; gq.delta = delta;
+  gq.dk_self = dk_self; gq.dv_self = dv_self; gq.scale = scale;
+  BwdArgs gk = gq;
+  gq.a = aq; gq.bm = bm_q;
+  gk.a = ak; gk.bm = bm_k;
+  // one workgroup per 128-row sub-tile of every item
+  grid_q *= bm_q / kBwdRows;
+  grid_k *= bm_k / kBwdRows;
   switch (d) {
-    case 64: return go<64>(g, grid, s);
-    case 128: return go<128>(g, grid, s);
+    case 64: return go<64>(gq, grid_q, gk, grid_k, s);
+    case 128: return go<128>(gq, grid_q, gk, grid_k, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -310,9 +310,12 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma_self_planned(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
-hipError_t launch_attn_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dk,
-                           void* dv, float* delta, float scale, int d, int bm, int64_t grid,
-                           hipStream_t s);
+// the backward: k_bwd_dq over plan aq (tiles of bm_q query rows), k_bwd_dkdv over plan ak
+// (its items read as key tiles; the same plan in full mode, a key-major one in a
+// candidate-only layer)
+hipError_t launch_attn_bwd(const AttnArgs& aq, int bm_q, int64_t grid_q, const AttnArgs& ak, int bm_k,
+                           int64_t grid_k, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* dk_self, void* dv_self, float* delta, float scale, int d, hipStream_t s);
 hipError_t launch_rope_positions(const int32_t* offsets, const int32_t* cand_start,
                                  const int32_t* pos_base, int B, int T, int32_t* pos, hipStream_t s);
 hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, const int32_t* offsets,

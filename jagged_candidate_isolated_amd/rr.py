@@ -59,6 +59,11 @@ _SIGS = {
     "rr_ranker_cached_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "rr_ranker_cached_fwd": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                             ctypes.c_size_t, _P]),
+    "rr_cand_only_run_lse": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
+                                            ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_cand_only_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "rr_cand_only_bwd_run": (ctypes.c_int, [_P] * 15 + [_I, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float, _P,
+                                                        ctypes.c_size_t, _P]),
     "rr_cand_only_plan": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P,
                                          ctypes.c_size_t, _P]),
     "rr_cand_only_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
@@ -614,3 +619,66 @@ def rr_ranker_cached_workspace_bytes(B: int, Th: int, Tc: int, H: int, d: int) -
 def rr_forward_fingerprint() -> str:
     """Digest of the forward attention kernels' machine code in the loaded library."""
     return _lib.rr_forward_fingerprint().decode()
+
+
+def rr_cand_only_bwd_workspace_bytes(B: int, Th: int, Tc: int, H: int, d: int) -> int:
+    return int(_lib.rr_cand_only_bwd_workspace_bytes(B, Th, Tc, H, d))
+
+
+def rr_cand_only_train_plan(hist_offsets, cand_offsets, Th: int, Tc: int, H: int, d: int, dtype, stream=None):
+    """rr_cand_only_plan into a workspace sized for the backward as well."""
+    dev = cand_offsets.device
+    B = cand_offsets.numel() - 1
+    ws = _workspace(rr_cand_only_bwd_workspace_bytes(B, Th, Tc, H, d), None, dev)
+    return rr_cand_only_plan(hist_offsets, cand_offsets, Th, Tc, H, d, dtype, workspace=ws, stream=stream)
+
+
+def rr_cand_only_run_lse(q_cand, k_hist, v_hist, k_cand, v_cand, B: int, workspace, scale=None, out=None,
+                         lse=None, stream=None):
+    """rr_cand_only_run that also returns each candidate row's log-sum-exp: (out, lse [Tc, H])."""
+    dev = q_cand.device
+    _need(q_cand, "q_cand")
+    dt = _rr_dtype(q_cand)
+    Tc, H, d = q_cand.shape
+    Th = k_hist.shape[0]
+    for name, t in (("k_hist", k_hist), ("v_hist", v_hist), ("k_cand", k_cand), ("v_cand", v_cand)):
+        _need(t, name, q_cand.dtype, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if out is None:
+        out = torch.empty_like(q_cand)
+    if lse is None:
+        lse = torch.empty((Tc, H), dtype=torch.float32, device=dev)
+    _need(out, "out", q_cand.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _check("rr_cand_only_run_lse", _lib.rr_cand_only_run_lse(
+        _ptr(q_cand), _ptr(k_hist), _ptr(v_hist), _ptr(k_cand), _ptr(v_cand), _ptr(out), _ptr(lse), B, Th, Tc, H,
+        d, dt, float(scale or 0.0), _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return out, lse
+
+
+def rr_cand_only_bwd_run(q_cand, k_hist, v_hist, k_cand, v_cand, o_cand, dout, lse, hist_offsets, cand_offsets,
+                         workspace, scale=None, stream=None):
+    """Gradients of a candidate-only layer: (dq_cand, dk_hist, dv_hist, dk_cand, dv_cand)."""
+    dev = q_cand.device
+    _need(q_cand, "q_cand")
+    dt = _rr_dtype(q_cand)
+    Tc, H, d = q_cand.shape
+    Th = k_hist.shape[0]
+    for name, t in (("k_cand", k_cand), ("v_cand", v_cand), ("o_cand", o_cand), ("dout", dout)):
+        _need(t, name, q_cand.dtype, dev)
+        if t.shape != q_cand.shape:
+            raise ValueError(f"{name} must be [Tc, H, d]")
+    for name, t in (("k_hist", k_hist), ("v_hist", v_hist)):
+        _need(t, name, q_cand.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _need(hist_offsets, "hist_offsets", torch.int32, dev)
+    _need(cand_offsets, "cand_offsets", torch.int32, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    B = cand_offsets.numel() - 1
+    grads = [torch.empty_like(q_cand), torch.empty_like(k_hist), torch.empty_like(v_hist), torch.empty_like(k_cand),
+             torch.empty_like(v_cand)]
+    _check("rr_cand_only_bwd_run", _lib.rr_cand_only_bwd_run(
+        _ptr(q_cand), _ptr(k_hist), _ptr(v_hist), _ptr(k_cand), _ptr(v_cand), _ptr(o_cand), _ptr(dout), _ptr(lse),
+        *[_ptr(g) for g in grads], _ptr(hist_offsets), _ptr(cand_offsets), B, Th, Tc, H, d, dt,
+        float(scale or 0.0), _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return tuple(grads)

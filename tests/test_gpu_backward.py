@@ -171,3 +171,89 @@ def test_backward_full_size_sampled_users(cfg):
         ref, es = _one_user(fb, b, h, got["dout"])
         for name, t, r, e in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, es):
             assert_close_grad(_np(t[lo:hi, h:h + 1]), r, e, f"config {cfg} user {b} head {h} {name}")
+
+
+# ---------------------------------------------------------------- candidate-only layers
+
+def _cand_only_train(cb, do_seed):
+    from _gpu import cand_only_dev
+    dv = cand_only_dev(cb)
+    Tc, H, d = cb.q_cand.shape
+    dout = W.draw_output_grad(do_seed, Tc, H, d, cb.dtype)
+    dout_d = to_dev(dout, torch_dtype(cb.dtype))
+    ws = rr().rr_cand_only_train_plan(dv["hist_offsets"], dv["cand_offsets"], cb.Th, Tc, H, d, dv["q_cand"].dtype)
+    o, lse = rr().rr_cand_only_run_lse(dv["q_cand"], dv["k_hist"], dv["v_hist"], dv["k_cand"], dv["v_cand"], cb.B, ws)
+    grads = rr().rr_cand_only_bwd_run(dv["q_cand"], dv["k_hist"], dv["v_hist"], dv["k_cand"], dv["v_cand"], o,
+                                      dout_d, lse, dv["hist_offsets"], dv["cand_offsets"], ws)
+    torch.cuda.synchronize()
+    return dout, grads, o
+
+
+def _check_cand_only(cb, dout, grads, what):
+    args = (cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand, dout, cb.hist_offsets, cb.cand_offsets)
+    ref = BW.cand_only_attention_backward(*args)
+    es = BW.cand_only_gradient_error_scale(*args)
+    for name, g, r, e in zip(("dq_cand", "dk_hist", "dv_hist", "dk_cand", "dv_cand"), grads, ref, es):
+        assert_close_grad(_np(g), r, e, f"{what} {name}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_cand_only_backward(d):
+    """Every gradient of a candidate-only layer: users with a long history, none, no
+    candidates, one candidate; against the oracle under the rounding bound; history keys of
+    users without candidates get exactly 0."""
+    rng = np.random.default_rng(8000 + d)
+    cb = W.make_cand_only_batch(rng, "co-bwd", hist=[300, 0, 45, 700, 129], cand=[37, 6, 0, 128, 1], H=3, d=d,
+                                scaled=False, seed=8100 + d)
+    dout, grads, _ = _cand_only_train(cb, 8200 + d)
+    _check_cand_only(cb, dout, grads, f"cand-only d={d}")
+    lo, hi = int(cb.hist_offsets[2]), int(cb.hist_offsets[3])
+    assert not _np(grads[1])[lo:hi].any() and not _np(grads[2])[lo:hi].any()
+    again = _cand_only_train(cb, 8200 + d)[1]
+    for a, b in zip(grads, again):
+        assert torch.equal(a, b), "repeated calls differ"
+
+
+def test_cand_only_backward_matches_full_candidate_rows():
+    """A candidate's dq and its own key's and value's gradients are bit for bit those the
+    full-sequence backward gives its row (the layer's fallback)."""
+    rng = np.random.default_rng(8300)
+    fb = W.make_full_batch(rng, "co-vs-full", prefix=[4, 2, 0, 3], hist=[300, 0, 45, 700], cand=[37, 6, 0, 128],
+                           H=2, d=128, scaled=False, seed=8301)
+    full = _train_step(fb, 8302)
+    cb = W.split_to_cand_only(fb)
+    cr = cb.meta["cand_rows"]
+    from _gpu import cand_only_dev
+    dv = cand_only_dev(cb)
+    Tc, H, d = cb.q_cand.shape
+    dout_d = to_dev(full["dout"][cr], torch.bfloat16)
+    ws = rr().rr_cand_only_train_plan(dv["hist_offsets"], dv["cand_offsets"], cb.Th, Tc, H, d, torch.bfloat16)
+    o, lse = rr().rr_cand_only_run_lse(dv["q_cand"], dv["k_hist"], dv["v_hist"], dv["k_cand"], dv["v_cand"], cb.B, ws)
+    g = rr().rr_cand_only_bwd_run(dv["q_cand"], dv["k_hist"], dv["v_hist"], dv["k_cand"], dv["v_cand"], o, dout_d,
+                                  lse, dv["hist_offsets"], dv["cand_offsets"], ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(o), full["o"][cr])
+    assert np.array_equal(_np(g[0]), full["dq"][cr])
+    assert np.array_equal(_np(g[3]), full["dk"][cr]) and np.array_equal(_np(g[4]), full["dv"][cr])
+
+
+def test_cand_only_backward_config4_sampled_users():
+    """The candidate-only workload (B=512, frozen histories up to 4000 rows, 512 candidates
+    each, H=8, d=128) at full size; whole users (one head each) against the oracle."""
+    cb = W.config4()
+    dout, grads, _ = _cand_only_train(cb, 8400)
+    hl = np.diff(cb.hist_offsets)
+    order = np.argsort(hl, kind="stable")
+    rng = np.random.default_rng(4)
+    for b in sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])}):
+        hs = slice(int(cb.hist_offsets[b]), int(cb.hist_offsets[b + 1]))
+        cs = slice(int(cb.cand_offsets[b]), int(cb.cand_offsets[b + 1]))
+        h = int(rng.integers(0, cb.H))
+        sub = [x[s, h:h + 1] for x, s in ((cb.q_cand, cs), (cb.k_hist, hs), (cb.v_hist, hs), (cb.k_cand, cs),
+                                           (cb.v_cand, cs))]
+        args = (*sub, dout[cs, h:h + 1], [0, hs.stop - hs.start], [0, cs.stop - cs.start])
+        ref = BW.cand_only_attention_backward(*args)
+        es = BW.cand_only_gradient_error_scale(*args)
+        for name, gt, s, r, e in zip(("dq_cand", "dk_hist", "dv_hist", "dk_cand", "dv_cand"), grads,
+                                     (cs, hs, hs, cs, cs), ref, es):
+            assert_close_grad(_np(gt[s, h:h + 1]), r, e, f"config 4 user {b} head {h} {name}")
