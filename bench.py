@@ -168,10 +168,15 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
 
     if cfg == 4:
         base = [up(b.q_cand, dt), up(b.k_hist, dt), up(b.v_hist, dt), up(b.k_cand, dt), up(b.v_cand, dt)]
+        if backward:
+            import workloads as W
+            base.append(up(W.draw_output_grad(b.seed + 77, b.Tc, b.H, b.d, b.dtype), dt))
         hoff, coff = up(b.hist_offsets), up(b.cand_offsets)
         out_like = base[0]
         Th, Tc, H, d = b.Th, b.Tc, b.H, b.d
-        ws = torch.empty(rr.rr_cand_only_workspace_bytes(b.B, Th, Tc, H, d), dtype=torch.uint8, device=dev)
+        nbytes = (rr.rr_cand_only_bwd_workspace_bytes if backward else rr.rr_cand_only_workspace_bytes)(b.B, Th, Tc,
+                                                                                                       H, d)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     else:
         base = [up(b.q, dt), up(b.k, dt), up(b.v, dt)]
         if backward:
@@ -188,8 +193,8 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
     copies = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
     sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
     outs = [torch.empty_like(out_like) for _ in range(copies)]
-    grads = [[torch.empty_like(out_like) for _ in range(3)] for _ in range(copies)] if backward else None
-    lse = torch.empty((b.T, b.H), dtype=torch.float32, device=dev) if backward else None
+    grads = [[torch.empty_like(out_like) for _ in range(3)] for _ in range(copies)] if backward and cfg != 4 else None
+    lse = torch.empty((b.Tc if cfg == 4 else b.T, b.H), dtype=torch.float32, device=dev) if backward else None
 
     # rotary q / k land in one set of buffers that the attention of the same step reads
     rot = [torch.empty_like(t) for t in base] if rope else None
@@ -206,11 +211,18 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
             rr.rr_rope_qk(None, s[1], hoff, hist_end, k_out=rot[1])
             rr.rr_rope_qk(s[0], s[3], coff, cand_first, pos_base=hist_len, q_out=rot[0], k_out=rot[3])
 
+        def bwd_only(i):
+            s = sets[i % copies]
+            rr.rr_cand_only_bwd_run(s[0], s[1], s[2], s[3], s[4], outs[i % copies], s[5], lse, hoff, coff, ws)
+
         def run(i):
             s = sets[i % copies]
             if rope:
                 rope_only(i)
                 rr.rr_cand_only_run(rot[0], rot[1], s[2], rot[3], s[4], b.B, ws, out=outs[i % copies])
+            elif backward:
+                rr.rr_cand_only_run_lse(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies], lse=lse)
+                bwd_only(i)
             else:
                 rr.rr_cand_only_run(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies])
     elif self_planned(b) and not rope and not backward:
@@ -258,14 +270,18 @@ def cpu_baseline(cfg, b, budget_s, rope=False, backward=False):
     from oracle import backward as BW
     from oracle import rotary as RO
     full_fn = RO.full_attention_rope if rope else A.full_attention
+    cand_fn = RO.cand_only_attention_rope if rope else A.cand_only_attention
     if backward:
         import workloads as W
-        dout = W.draw_output_grad(b.seed + 77, b.T, b.H, b.d, b.dtype)
+        dout = W.draw_output_grad(b.seed + 77, b.Tc if cfg == 4 else b.T, b.H, b.d, b.dtype)
 
         def full_fn(q, k, v, offsets, cand_start, valid, flag, rows=slice(None)):
             A.full_attention(q, k, v, offsets, cand_start, valid, flag)
             BW.full_attention_backward(q, k, v, dout[rows], offsets, cand_start, valid, flag)
-    cand_fn = RO.cand_only_attention_rope if rope else A.cand_only_attention
+
+        def cand_fn(qc, kh, vh, kc, vc, hoff, coff, rows=slice(None)):
+            A.cand_only_attention(qc, kh, vh, kc, vc, hoff, coff)
+            BW.cand_only_attention_backward(qc, kh, vh, kc, vc, dout[rows], hoff, coff)
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -281,13 +297,15 @@ def cpu_baseline(cfg, b, budget_s, rope=False, backward=False):
         while time.perf_counter() - t0 < budget_s and users < b.B:
             u = users
             sl = slice(int(coff[u]), int(coff[u + 1]))
+            extra = {"rows": sl} if backward else {}
             cand_fn(b.q_cand[sl], b.k_hist[int(hoff[u]):int(hoff[u + 1])],
-                                  b.v_hist[int(hoff[u]):int(hoff[u + 1])], b.k_cand[sl], b.v_cand[sl],
-                                  [0, int(hl[u])], [0, int(cl[u])])
+                    b.v_hist[int(hoff[u]):int(hoff[u + 1])], b.k_cand[sl], b.v_cand[sl],
+                    [0, int(hl[u])], [0, int(cl[u])], **extra)
             done_flops += acc.attention_flops(acc.cand_only_pairs([hl[u]], [cl[u]]), b.H, b.d)
             done_cands += int(cl[u])
             users += 1
-        sample = f"first {users} of {b.B} users, candidate-only oracle" + (" with rotary q/k" if rope else "")
+        sample = (f"first {users} of {b.B} users, candidate-only oracle" + (" with rotary q/k" if rope else "")
+                  + (", forward + backward" if backward else ""))
     else:
         eff_all, _ = acc.full_mode_counts(b.prefix, b.hist, b.cand, b.pad, b.attend_padded_history)
         small = b.T <= 40000
@@ -487,9 +505,9 @@ def main():
             sys.exit(2)
         run_ranker(args, b, torch, rr)
         return
-    if args.backward and (cfg == 4 or b.dtype != "bf16" or b.d not in (64, 128) or args.rope):
-        print("--backward runs the full-sequence bf16 workloads with d 64 or 128 (configs 2, 3, 5, 6, 7), "
-              "without --rope", file=sys.stderr)
+    if args.backward and (b.dtype != "bf16" or b.d not in (64, 128) or args.rope):
+        print("--backward runs the bf16 workloads with d 64 or 128 (configs 2 to 7), without --rope",
+              file=sys.stderr)
         sys.exit(2)
     eff_flops, exec_flops, alg_bytes, n_cands = work_counts(cfg, b)
     fwd_eff, fwd_exec = eff_flops, exec_flops
