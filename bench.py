@@ -143,6 +143,27 @@ def work_counts(cfg, b):
             acc.full_mode_bytes(b.T, b.H, b.d, es), int(b.cand.sum()))
 
 
+def mfma_executed_flops(cfg, b):
+    """FLOPs the forward kernel issues on the matrix cores for one step: every query tile
+    (128 rows, or 256 when users average 2048 rows or more) runs whole over key blocks of 64
+    columns (128 at d = 32), both products (S = K Q^T and O = V^T P^T) at 2 d FLOPs per
+    pair; the library's tile rule.  None off the MFMA kernel (fp32, d = 16)."""
+    import numpy as np
+    from jagged_candidate_isolated_amd import accounting as acc
+    if b.dtype != "bf16" or b.d < 32:
+        return None
+    bn = 128 if b.d == 32 else 64
+    if cfg == 4:
+        n_q, n_kv, rows = np.diff(b.cand_offsets), np.diff(b.hist_offsets), b.Tc
+    else:
+        pad = b.pad if b.attend_padded_history else 0
+        n_kv = b.prefix + pad + b.hist
+        n_q = n_kv + b.cand
+        rows = b.T
+    bm = 256 if rows >= 2048 * b.B else 128
+    return acc.attention_flops(acc.tile_pairs(n_q, n_kv, bm, bn), b.H, b.d)
+
+
 def self_planned(b) -> bool:
     """Whether rr_attn_fwd plans this batch inside the attention kernel (a small unpadded
     bf16 batch: at most 256 users, at most 1024 workgroups); the library's rule."""
@@ -578,17 +599,19 @@ def main():
             print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
             g = None
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps_k + 1)]
+        ev[0].record(stream)
         for r in range(reps_k):
             if g is not None:
                 g.replay()
             else:
                 for i in range(n_run):
                     fn(i)
-        e1.record(stream)
+            ev[r + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps_k * n_run)
+        per = [ev[r].elapsed_time(ev[r + 1]) / n_run for r in range(reps_k)]
+        time_launches.median = float(np.median(per))
+        return ev[0].elapsed_time(ev[-1]) / (reps_k * n_run)
 
     if args.rope:
         rope_ms = time_launches(rope_only)
@@ -598,6 +621,7 @@ def main():
         kernel_ms = time_launches(run) - bwd_ms      # the forward of the training step
     else:
         kernel_ms = time_launches(run)
+        kernel_ms_median = time_launches.median
     # the roofline entry covers the forward kernel
     eff_flops_all, exec_flops_all = eff_flops, exec_flops
     eff_flops, exec_flops = fwd_eff, fwd_exec
@@ -618,6 +642,8 @@ def main():
     roof["kernel"] = "k_attn_mfma" if b.dtype == "bf16" and b.d >= 32 else "k_attn_simple"
     roof["self_planned"] = bool(cfg != 4 and self_planned(b) and not args.rope and not args.backward)
     roof["kernel_ms"] = kernel_ms
+    if not (args.rope or args.backward):
+        roof["kernel_ms_median"] = kernel_ms_median
     roof["alg_bytes"] = alg_bytes
     roof["alg_flops"] = exec_flops
 
@@ -632,7 +658,16 @@ def main():
         "input_copies_rotated": copies, "footprint_bytes": footprint,
         "timing": "hip graph replay" if graph is not None else "eager launches",
         "roofline": roof,
+        # the forward kernel against both ceilings, whichever bounds it
+        "fractions": {"mfma": (exec_flops / (kernel_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+                               if b.dtype == "bf16" else None),
+                      "hbm": alg_bytes / (kernel_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
     }
+    mfma_flops = mfma_executed_flops(cfg, b)
+    if mfma_flops:
+        out["mfma_efficiency"] = {"effective_flops": eff_flops, "mfma_flops": mfma_flops,
+                                  "ratio": eff_flops / mfma_flops,
+                                  "mfma_tflops": mfma_flops / (kernel_ms / 1e3) / 1e12}
     if args.rope:
         es = 2 if b.dtype == "bf16" else 4
         rows_qk = (b.Tc + b.Th + b.Tc) if cfg == 4 else 2 * b.T      # rows of q and k rotated

@@ -73,3 +73,13 @@ def cand_only_pairs(hist, cand) -> int:
 
 def cand_only_bytes(Th: int, Tc: int, H: int, d: int, elem_bytes: int) -> int:
     return (2 * Th + 4 * Tc) * H * d * elem_bytes
+
+
+def tile_pairs(n_q, n_kv, bm: int, bn: int) -> int:
+    """(query, key) pairs the matrix cores execute per head when each user's n_q query rows
+    go in tiles of bm rows and each tile loops over the user's n_kv keys in blocks of bn
+    columns: the last query tile and the last key block run whole.  Users without queries
+    or without keys run no key block."""
+    q = np.asarray(n_q, np.int64)
+    k = np.asarray(n_kv, np.int64)
+    return int(np.sum(-(-q // bm) * bm * (-(-k // bn) * bn)))

@@ -40,3 +40,23 @@ def test_isolation_pairs_match_mask_count():
         seg = J.segment_ids(offs, cs)
         admitted = sum(int(A.isolation_mask(seg[offs[b]:offs[b + 1]]).sum()) for b in range(B))
         assert admitted == acc.isolation_pairs(P + h, c)
+
+
+def test_tile_pairs_brute_force():
+    """Tile-padded pair count against enumeration of every (tile row, tile column) pair."""
+    rng = np.random.default_rng(4)
+    for _ in range(30):
+        B = int(rng.integers(1, 5))
+        n_q = rng.integers(0, 300, B)
+        n_kv = rng.integers(0, 200, B)
+        bm, bn = int(rng.choice([32, 128, 256])), int(rng.choice([32, 64, 128]))
+        want = 0
+        for q, k in zip(n_q, n_kv):
+            rows = sum(bm for t in range(0, int(q), bm))
+            cols = sum(bn for t in range(0, int(k), bn))
+            want += rows * cols
+        assert acc.tile_pairs(n_q, n_kv, bm, bn) == want
+    # exact tiles waste nothing; one row or key over a tile costs a whole tile
+    assert acc.tile_pairs([256], [128], 128, 64) == 256 * 128
+    assert acc.tile_pairs([257], [129], 128, 64) == 384 * 192
+    assert acc.tile_pairs([0, 5], [7, 0], 128, 64) == 0
