@@ -69,8 +69,8 @@ const char* rr_status_string(int status);
 /* Library ABI version (increments when a signature changes). */
 int rr_abi_version(void);
 
-/* Digest of the forward attention kernels' gfx950 machine code in this build: equal
- * digests mean equal forward kernels, so a profile taken on one build applies to another. */
+/* Digest of the forward attention kernels' gfx950 machine code in the loaded library: equal
+ * digests mean equal forward kernels, so a profile taken with one library applies to another. */
 const char* rr_forward_fingerprint(void);
 
 /*
