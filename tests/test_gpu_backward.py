@@ -173,6 +173,27 @@ def test_backward_full_size_sampled_users(cfg):
             assert_close_grad(_np(t[lo:hi, h:h + 1]), r, e, f"config {cfg} user {b} head {h} {name}")
 
 
+def _many_users_batch(seed, d=64):
+    """More users (2300) than the work-list builder sorts in LDS: the plans keep the user
+    order and read the per-user counts back from global memory."""
+    rng = np.random.default_rng(seed)
+    B = 2300
+    P = rng.integers(0, 3, B)
+    h = rng.integers(0, 40, B) * (rng.random(B) > 0.1)
+    c = rng.integers(0, 6, B) * (rng.random(B) > 0.1)
+    h[::97] = 130
+    c[::89] = 131
+    return W.make_full_batch(rng, f"bwd-many{seed}", prefix=P, hist=h, cand=c, H=2, d=d, scaled=False,
+                             seed=seed + 1)
+
+
+def test_backward_more_users_than_the_lds_sort():
+    fb = _many_users_batch(7100)
+    print(f"[backward, many users] B={fb.B} T={fb.T}", flush=True)
+    got = _train_step(fb, 7102)
+    _check_grads(fb, got, f"{fb.B} users")
+
+
 # ---------------------------------------------------------------- candidate-only layers
 
 def _cand_only_train(cb, do_seed):
@@ -235,6 +256,13 @@ def test_cand_only_backward_matches_full_candidate_rows():
     assert np.array_equal(_np(o), full["o"][cr])
     assert np.array_equal(_np(g[0]), full["dq"][cr])
     assert np.array_equal(_np(g[3]), full["dk"][cr]) and np.array_equal(_np(g[4]), full["dv"][cr])
+
+
+def test_cand_only_backward_more_users_than_the_lds_sort():
+    cb = W.split_to_cand_only(_many_users_batch(7200, d=128))
+    print(f"[candidate-only backward, many users] B={cb.B} Th={cb.Th} Tc={cb.Tc}", flush=True)
+    dout, grads, _ = _cand_only_train(cb, 7202)
+    _check_cand_only(cb, dout, grads, f"candidate-only, {cb.B} users")
 
 
 def test_cand_only_backward_config4_sampled_users():

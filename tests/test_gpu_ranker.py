@@ -193,6 +193,27 @@ def test_cached_request_bit_identical():
     assert torch.equal(cached, xc2)
 
 
+def test_many_users_cached_request_bit_identical():
+    """2200 users (more than the plans sort in LDS, several passes of the split's per-user
+    scan): the cached request still reproduces the full request bit for bit."""
+    rng = np.random.default_rng(62)
+    B = 2200
+    shapes = dict(prefix=rng.integers(0, 3, B), hist=rng.integers(0, 40, B) * (rng.random(B) > 0.1),
+                  cand=rng.integers(0, 6, B) * (rng.random(B) > 0.1))
+    shapes["hist"][::97] = 130
+    shapes["cand"][::89] = 131
+    H, d, n_layers, nco = 2, 64, 2, 1
+    x, off, cs, dl, _ = _setup(H, d, n_layers, seed=63, shapes=shapes)
+    print(f"[ranker, many users] B={B} T={int(off[-1])}", flush=True)
+    _, xc, xh, cache = _run(x, off, cs, dl, nco, H, d)
+    xh0, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    again = rr().rr_ranker_cached_fwd(to_dev(xc0.astype(np.float32)), dl, cache, to_dev(hoff.astype(np.int32)),
+                                      to_dev(coff.astype(np.int32)), H, d)
+    torch.cuda.synchronize()
+    assert torch.equal(again, xc)
+    assert np.all(np.isfinite(_np(xc))) and np.all(np.isfinite(_np(xh)))
+
+
 def test_candidate_order_bit_identical():
     H, d, n_layers, nco = 4, 64, 3, 1
     x, off, cs, dl, _ = _setup(H, d, n_layers, seed=70)
