@@ -72,7 +72,8 @@ struct GemmArgs {
 };
 
 template <int EPI, int WM, int WN, int TM, int TN, int NS>
-__global__ __launch_bounds__(WM * WN * 64, (WM * WN == 4 && TM * TN == 4 && NS == 2) ? 2 : 1) void k_gemm_bt(
+__global__ __launch_bounds__(WM * WN * 64, (WM * WN >= 8 || (WM * WN == 4 && TM * TN == 4 && NS == 2)) ? 2 : 1)
+    void k_gemm_bt(
     GemmArgs g) {
   constexpr int kThr = WM * WN * 64, BMt = WM * TM * 32, BNt = WN * TN * 32;
   constexpr int LA = BMt * kGch / kThr, LW = BNt * kGch / kThr;   // 16-byte loads per thread and K step
@@ -354,8 +355,15 @@ hipError_t launch_gemm_bt(const void* a, const void* w, int M, int N, int K, voi
   for (int i = 0; i < 3; ++i) g.out[i] = out ? static_cast<u16*>(out[i]) : nullptr;
   g.out_cols = out_cols;
   g.res = res;
-  // 128 x 128 tiles of 4 waves (64 x 64 each): 128 x 256 (4 waves of 64 x 128) and
-  // 256 x 128 (8 waves) measured 5-10% and 1-3% slower on the layer stack
+  // Large products: 256 x 256 tiles of 8 waves, 128 x 64 each (two waves per SIMD, one
+  // workgroup per CU; each LDS operand read feeds 1.33 MFMAs instead of 1), used when
+  // they fill the chip at least twice over.  Smaller ones: 128 x 128 tiles of 4 waves,
+  // 64 x 64 each.  Every element's sum runs through the same MFMA sequence at the same
+  // position of a 32 x 32 block in both shapes, so a row's result never depends on the
+  // shape chosen, i.e. on the other rows of the launch.
+  constexpr int64_t kFill = 512;
+  if (N % 256 == 0 && int64_t((M + 255) / 256) * (N / 256) >= kFill)
+    return gemm_go<2, 4, 4, 2, RR_GEMM_STAGES>(g, s);
   return gemm_go<2, 2, 2, 2, RR_GEMM_STAGES>(g, s);
 }
 

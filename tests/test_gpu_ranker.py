@@ -75,6 +75,34 @@ def test_linear_bounds_and_rows():
         assert np.array_equal(_np(one)[0], got[r])
 
 
+def test_linear_large_tile_rows():
+    """A product large enough for the 256 x 256 tiles: sampled rows within the rounding
+    bound, and every row bit-identical to the same row computed in a small launch (the
+    128 x 128 tiles), plus a slice of rows at an offset that is not a tile multiple."""
+    rng = np.random.default_rng(3)
+    M, N, K = 65536, 512, 256
+    a = W.round_to_bf16(rng.standard_normal((M, K)).astype(np.float32)).astype(np.float64)
+    w = W.round_to_bf16((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)).astype(np.float64)
+    ad, wd = to_dev(a, torch.bfloat16), to_dev(w, torch.bfloat16)
+    big = rr().rr_linear(ad, wd)
+    rows = np.sort(rng.choice(M, 300, replace=False))
+    got = _np(big[torch.from_numpy(rows).to(big.device)])
+    ref = a[rows] @ w.T
+    mag = np.abs(a[rows]) @ np.abs(w).T
+    assert np.all(np.abs(got - ref) <= U * np.abs(ref) + (K + 2) * F32 * mag)
+    for lo, n in ((0, 1), (777, 130), (M - 40, 40)):
+        part = rr().rr_linear(ad[lo:lo + n].contiguous(), wd)
+        torch.cuda.synchronize()
+        assert torch.equal(part, big[lo:lo + n]), (lo, n)
+    res0 = to_dev(rng.standard_normal((M, N)).astype(np.float32))
+    res = res0.clone()
+    rr().rr_linear(ad, wd, residual=res)
+    part = res0[777:907].clone()
+    rr().rr_linear(ad[777:907].contiguous(), wd, residual=part)
+    torch.cuda.synchronize()
+    assert torch.equal(part, res[777:907])
+
+
 def test_rms_norm_bounds():
     rng = np.random.default_rng(2)
     x = (rng.standard_normal((37, 256)) * rng.uniform(0.01, 20, (37, 1))).astype(np.float32)
