@@ -27,7 +27,7 @@
 // Pipeline.  K and V tiles go to LDS by direct-to-LDS loads (no register staging)
 // into NS rotating buffers, NS-1 tiles ahead of the tile being computed; one
 // barrier per tile.  Two tile shapes: narrow (four waves, 128 query rows, two stages,
-// two workgroups per CU) and wide (eight waves, 256 query rows, four stages, one
+// two to four workgroups per CU) and wide (eight waves, 256 query rows, four stages, one
 // workgroup per CU) for batches of long users.  A small unpadded batch can skip the
 // planning kernel: each workgroup then builds the work list itself (self_plan_item).
 //
@@ -321,8 +321,9 @@ hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
 
 }  // namespace
 
-// Tile shapes (compile-time tuning knobs).  Narrow: four waves, 128 query rows, two
-// workgroups per CU.  Wide: eight waves, 256 query rows, one workgroup per CU.
+// Tile shapes (compile-time tuning knobs).  Narrow: four waves, 128 query rows, four
+// workgroups per CU at d = 32 and 64, two at d = 128 (registers).  Wide: eight waves,
+// 256 query rows, one workgroup per CU.
 #ifndef RR_NARROW_STAGES
 #define RR_NARROW_STAGES 2
 #endif
