@@ -99,35 +99,47 @@ __device__ __forceinline__ v4i32 byte_range(const void* base, uint32_t bytes) {
 // stage being filled from the stage being read, would wait for every load in
 // flight before LDS reads and so empty the tile pipeline.  The kernels order these
 // loads themselves, with counted waits (wait_vmem) before each tile's barrier.
-// `lds_addr` is wave-uniform; m0 carries it to the load.
+// `lds_addr` is wave-uniform; m0 carries it to the load.  m0 is a register the
+// compiler reserves, so each block saves it, sets it (one wait state before the
+// load reads it) and restores it once the load has issued (the load takes m0 at
+// issue).
 __device__ __forceinline__ void lds_dma_buffer16(v4i32 rsrc, uint32_t voffset, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-      : "memory", "m0");
+      : "memory");
 }
 __device__ __forceinline__ void lds_dma_global16(const void* gptr, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
-      :
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "s"(lds_addr), "v"(gptr)
-      : "memory", "m0");
+      : "memory");
 }
 
 // 4-byte variant: lane l writes its 4 bytes to lds_addr + 4 l.
 __device__ __forceinline__ void lds_dma_global4(const void* gptr, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off"
-      :
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "s"(lds_addr), "v"(gptr)
-      : "memory", "m0");
+      : "memory");
 }
 
 // LDS address (byte offset in the workgroup's LDS) of a __shared__ location.
