@@ -282,6 +282,24 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
     return plan, run, rope_only, bwd_only, copies, footprint
 
 
+def host_info() -> dict:
+    """The host the CPU baseline ran on: cores available to this process and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return {"host_cores_available": avail, "cpu_model": model}
+
+
 def cpu_baseline(cfg, b, budget_s, rope=False, backward=False):
     """The oracle, as it stands, on the host cores: whole batches (or the first users of one)
     repeated until about ``budget_s`` of CPU time; effective TFLOP/s of what it finished
@@ -357,7 +375,7 @@ def cpu_baseline(cfg, b, budget_s, rope=False, backward=False):
     if backward:
         done_flops *= 3.5                 # forward + backward (2.5x), as the GPU figure counts
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2), "candidates_per_s": done_cands / dt}
+            "sample": sample, "seconds": round(dt, 2), "candidates_per_s": done_cands / dt, **host_info()}
 
 
 RANKER_LAYERS, RANKER_CAND_ONLY = 8, 2
@@ -501,7 +519,8 @@ def ranker_cpu_baseline(b, x0, layers, budget_s, user_tokens=None):
         users += 1
     dt = time.perf_counter() - t0
     return {"value": cands / dt, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {users} of {b.B} users, float64 layer-stack oracle", "seconds": round(dt, 2)}
+            "sample": f"first {users} of {b.B} users, float64 layer-stack oracle", "seconds": round(dt, 2),
+            **host_info()}
 
 
 def main():
