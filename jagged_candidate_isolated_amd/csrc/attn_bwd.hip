@@ -29,10 +29,17 @@
 // key column per lane and accumulates dv^T = dO^T P and dk^T = q^T dS the same way.
 #include "mfma_tile.h"
 
-// Tuning knobs: k_bwd_dq's key tile per head dimension, and the smallest head dimension
-// whose k_bwd_dkdv reads V operands from LDS rather than registers.
+// Tuning knobs: k_bwd_dq's key tile per head dimension (at d = 64, 64 keys for launches
+// of at most RR_BWD_SMALL_GRID workgroups, whose longest items set the time, and
+// RR_BWD_DQ_BN64 otherwise), k_bwd_dkdv's query tile at d = 64, and the smallest head
+// dimension whose k_bwd_dkdv reads V operands from LDS rather than registers.  The
+// tiles change no result: every gradient accumulates the same 16-row MFMA steps in
+// the same order whatever the tile.
 #ifndef RR_BWD_DQ_BN64
 #define RR_BWD_DQ_BN64 32
+#endif
+#ifndef RR_BWD_SMALL_GRID
+#define RR_BWD_SMALL_GRID 2048
 #endif
 #ifndef RR_BWD_DQ_BN128
 #define RR_BWD_DQ_BN128 32
@@ -41,7 +48,7 @@
 #define RR_BWD_VLDS_MIN_D 128
 #endif
 #ifndef RR_BWD_DKDV_BQ64
-#define RR_BWD_DKDV_BQ64 32
+#define RR_BWD_DKDV_BQ64 64
 #endif
 
 namespace rr {
@@ -452,7 +459,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
 template <int D>
 hipError_t go(const BwdArgs& gq, int64_t grid_q, const BwdArgs& gk, int64_t grid_k, hipStream_t s) {
   constexpr int BN = D == 128 ? RR_BWD_DQ_BN128 : RR_BWD_DQ_BN64;   // key tile of k_bwd_dq (register budget)
-  hipError_t e = launch1(k_bwd_dq<D, BN>, grid_q, kBwdWaves * 64, s, gq);
+  hipError_t e = D == 64 && grid_q <= RR_BWD_SMALL_GRID
+                     ? launch1(k_bwd_dq<D, 64>, grid_q, kBwdWaves * 64, s, gq)
+                     : launch1(k_bwd_dq<D, BN>, grid_q, kBwdWaves * 64, s, gq);
   if (e != hipSuccess) return e;
   return launch1(k_bwd_dkdv<D>, grid_k, kBwdWaves * 64, s, gk);
 }

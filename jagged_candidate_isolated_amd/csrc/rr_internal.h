@@ -203,7 +203,7 @@ __device__ __forceinline__ bool self_plan_item(const int32_t* offsets, const int
   for (int i = tid; i < kBuckets; i += blockDim.x) s.hist[i] = 0;
   for (int i = tid; i < kSelfPlanUsers / 4; i += blockDim.x) s.bkt[i] = 0;
   __syncthreads();
-  int bkt = kBuckets - 1, cnt = 0;
+  int bkt = kBuckets - 1;
   if (tid < B) {   // row ranges clamped into [0, rows), as the planning kernel does
     const int lo = min(max(offsets[tid], 0), rows);
     const int hi = min(max(offsets[tid + 1], lo), rows);
@@ -211,7 +211,6 @@ __device__ __forceinline__ bool self_plan_item(const int32_t* offsets, const int
     s.lo[tid] = lo;
     s.nq[tid] = hi - lo;
     s.nkv[tid] = cs - lo;
-    cnt = H * ((hi - lo + bm - 1) / bm);
     bkt = cost_bucket(cs - lo);
     atomicOr(&s.bkt[tid >> 2], static_cast<uint32_t>(bkt) << (8 * (tid & 3)));
     atomicAdd(&s.hist[bkt], 1);
