@@ -459,9 +459,12 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void k_bwd_dkdv(BwdArgs g) {
 template <int D>
 hipError_t go(const BwdArgs& gq, int64_t grid_q, const BwdArgs& gk, int64_t grid_k, hipStream_t s) {
   constexpr int BN = D == 128 ? RR_BWD_DQ_BN128 : RR_BWD_DQ_BN64;   // key tile of k_bwd_dq (register budget)
-  hipError_t e = D == 64 && grid_q <= RR_BWD_SMALL_GRID
-                     ? launch1(k_bwd_dq<D, 64>, grid_q, kBwdWaves * 64, s, gq)
-                     : launch1(k_bwd_dq<D, BN>, grid_q, kBwdWaves * 64, s, gq);
+  hipError_t e;
+  if constexpr (D == 64)
+    e = grid_q <= RR_BWD_SMALL_GRID ? launch1(k_bwd_dq<D, 64>, grid_q, kBwdWaves * 64, s, gq)
+                                    : launch1(k_bwd_dq<D, BN>, grid_q, kBwdWaves * 64, s, gq);
+  else
+    e = launch1(k_bwd_dq<D, BN>, grid_q, kBwdWaves * 64, s, gq);
   if (e != hipSuccess) return e;
   return launch1(k_bwd_dkdv<D>, grid_k, kBwdWaves * 64, s, gk);
 }
