@@ -196,6 +196,41 @@ def test_cand_only_equals_full_mode_rows(d):
     assert np.array_equal(co, full[cb.meta["cand_rows"]])
 
 
+# ---------------------------------------------------------------- random small batches
+
+def test_random_batches_both_modes():
+    """Twenty-four random small batches (users, lengths, heads, head width, padding holes
+    and flag drawn per batch): every element of the full-sequence output against the
+    oracle, and for unpadded bf16 batches the candidate-only layer against the oracle and
+    bit for bit against the full mode's candidate rows."""
+    rng = np.random.default_rng(2024)
+    for i in range(24):
+        B = int(rng.integers(1, 12))
+        d = int(rng.choice([16, 32, 64, 128]))
+        dtype = "f32" if d == 16 or rng.random() < 0.25 else "bf16"
+        H = int(rng.integers(1, 5))
+        P = rng.integers(0, 4, B)
+        h = rng.integers(0, 200, B) * (rng.random(B) > 0.2)
+        c = rng.integers(0, 140, B) * (rng.random(B) > 0.2)
+        holes = bool(rng.random() < 0.3)
+        flag = bool(holes and rng.random() < 0.5)
+        lens = P + h + c
+        valid = (rng.random(int(lens.sum())) > 0.3).astype(np.uint8) if holes else None
+        fb = W.make_full_batch(rng, f"rand{i}", prefix=P, hist=h, cand=c, H=H, d=d, dtype=dtype,
+                               scaled=(dtype == "bf16"), valid=valid, attend_padded_history=flag,
+                               seed=9300 + i)
+        _log(f"[random {i}] B={B} T={fb.T} H={H} d={d} {dtype} holes={holes} flag={flag}")
+        full = run_full(fb)
+        assert_close(full, _oracle_full(fb), dtype, f"random batch {i}")
+        if not holes and dtype == "bf16":
+            cb = W.split_to_cand_only(fb)
+            co = run_cand_only(cb)
+            ref = A.cand_only_attention(cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand,
+                                        cb.hist_offsets, cb.cand_offsets)
+            assert_close(co, ref, dtype, f"random batch {i}, candidate-only")
+            assert np.array_equal(co, full[cb.meta["cand_rows"]]), f"random batch {i}"
+
+
 # ---------------------------------------------------------------- more users than the in-LDS sort
 
 # The work-list builder sorts up to 2048 users in LDS; larger batches keep the user order
