@@ -173,6 +173,33 @@ def test_backward_full_size_sampled_users(cfg):
             assert_close_grad(_np(t[lo:hi, h:h + 1]), r, e, f"config {cfg} user {b} head {h} {name}")
 
 
+def test_backward_random_batches():
+    """Twelve random small batches (users, lengths, heads, head width 64 or 128, padding
+    holes and flag drawn per batch): every gradient against the oracle under the rounding
+    bound; for unpadded batches also the candidate-only layer's gradients."""
+    rng = np.random.default_rng(2025)
+    for i in range(12):
+        B = int(rng.integers(1, 8))
+        d = int(rng.choice([64, 128]))
+        H = int(rng.integers(1, 4))
+        P = rng.integers(0, 4, B)
+        h = rng.integers(0, 180, B) * (rng.random(B) > 0.2)
+        c = rng.integers(0, 140, B) * (rng.random(B) > 0.2)
+        holes = bool(rng.random() < 0.3)
+        flag = bool(holes and rng.random() < 0.5)
+        lens = P + h + c
+        valid = (rng.random(int(lens.sum())) > 0.3).astype(np.uint8) if holes else None
+        fb = W.make_full_batch(rng, f"bwd-rand{i}", prefix=P, hist=h, cand=c, H=H, d=d, scaled=False,
+                               valid=valid, attend_padded_history=flag, seed=9400 + i)
+        print(f"[backward random {i}] B={B} T={fb.T} H={H} d={d} holes={holes} flag={flag}", flush=True)
+        got = _train_step(fb, 9500 + i)
+        _check_grads(fb, got, f"random batch {i}")
+        if not holes:
+            cb = W.split_to_cand_only(fb)
+            dout, grads, _ = _cand_only_train(cb, 9600 + i)
+            _check_cand_only(cb, dout, grads, f"random batch {i}, candidate-only")
+
+
 def _many_users_batch(seed, d=64):
     """More users (2300) than the work-list builder sorts in LDS: the plans keep the user
     order and read the per-user counts back from global memory."""
