@@ -1,11 +1,10 @@
 """Oracle: explicit-mask dense softmax attention in float64 (test infrastructure only).
 
 Candidate isolation attention mask page:
-  * section "段 ID：掩码的表达方式" gives the visibility rule from segment IDs:
-    history_mask = key is history and query is history or candidate;
-    candidate_self_mask = query and key are both candidates at the same position;
-    a query may read a key when either holds.
-  * section "掩码长什么样" prints the resulting table for P=1, H=3, C=3.
+  * section "段 ID：掩码的表达方式" gives who may read whom, in terms of segment IDs:
+    a query that is not padding reads every history key (segment 1) of its user, and a
+    candidate query reads, besides those, its own row and no other candidate;
+  * section "掩码长什么样" prints that rule as a table for P=1, H=3, C=3;
   * section "只更新候选的末尾层" describes candidate-only layers and their fallback
     (run the full layer, keep the candidate rows).
 No position reads another user's rows (HSTU scaling notes, section
@@ -31,19 +30,16 @@ def _scale(scale, d):
 
 
 def isolation_mask_rows(seg, rows) -> np.ndarray:
-    """Rows ``rows`` (local positions) of one user's [L, L] visibility mask from its segment IDs."""
+    """Rows ``rows`` (local positions) of one user's [L, L] visibility mask from its segment IDs:
+    every non-padding query row reads the user's history columns; a candidate row also reads
+    its own column."""
     seg = np.asarray(seg)
     rows = np.asarray(rows, dtype=np.int64)
-    L = len(seg)
-    q_is_history = (seg == 1)[rows]
-    q_is_candidate = (seg == -1)[rows]
-    kv_is_history = seg == 1
-    kv_is_candidate = seg == -1
-    q_pos = rows[:, None]
-    kv_pos = np.arange(L)[None, :]
-    history_mask = kv_is_history[None, :] & (q_is_history | q_is_candidate)[:, None]
-    candidate_self_mask = q_is_candidate[:, None] & kv_is_candidate[None, :] & (q_pos == kv_pos)
-    return history_mask | candidate_self_mask
+    role = seg[rows]
+    visible = np.outer(role != 0, seg == 1)
+    own = np.nonzero(role == -1)[0]
+    visible[own, rows[own]] = True
+    return visible
 
 
 def isolation_mask(seg) -> np.ndarray:

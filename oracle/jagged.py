@@ -25,30 +25,27 @@ def offsets_from_lengths(lengths) -> np.ndarray:
 def segment_ids(offsets, cand_start, valid=None, attend_padded_history=False) -> np.ndarray:
     """Per-row segment ID: 1 = valid prefix/history, -1 = valid candidate, 0 = padding.
 
-    Candidate isolation attention mask page, section "段 ID：掩码的表达方式":
-    a position is a candidate when it is at or after the candidate start
-    offset; its validity is the padding mask, widened by
-    ``attend_padded_history`` to every non-candidate position; valid positions
-    get -1 (candidate) or 1, invalid ones 0.
+    Candidate isolation attention mask page, section "段 ID：掩码的表达方式".  Each row
+    belongs to one user; the user's candidate block is every row from its candidate
+    start onward.  A row's role is "candidate" (-1) inside that block and "history" (1)
+    before it.  A row keeps its role when the padding mask marks it valid -- and, with
+    ``attend_padded_history``, every row before the candidate block keeps it too --
+    otherwise it is padding (0).
 
     ``offsets`` int [B+1]; ``cand_start`` int [B], absolute row of user b's first
     candidate; ``valid`` [T] truthy mask or None (= every row valid)."""
     offsets = np.asarray(offsets, dtype=np.int64)
     cand_start = np.asarray(cand_start, dtype=np.int64)
-    B = len(offsets) - 1
-    T = int(offsets[-1]) if B >= 0 else 0
-    seg = np.zeros(T, dtype=np.int8)
-    for b in range(B):
-        for idx in range(int(offsets[b]), int(offsets[b + 1])):
-            is_candidate = idx >= cand_start[b]
-            row_valid = True if valid is None else bool(valid[idx])
-            if attend_padded_history:
-                row_valid = row_valid or not is_candidate
-            if row_valid:
-                seg[idx] = -1 if is_candidate else 1
-            else:
-                seg[idx] = 0
-    return seg
+    n_users = len(offsets) - 1
+    n_rows = int(offsets[-1]) if n_users >= 0 else 0
+    owner = np.repeat(np.arange(n_users), np.diff(offsets))       # user of every row
+    row = np.arange(n_rows)
+    in_candidate_block = row >= cand_start[owner]
+    role = np.where(in_candidate_block, -1, 1)
+    kept = np.ones(n_rows, dtype=bool) if valid is None else np.asarray(valid).astype(bool)
+    if attend_padded_history:
+        kept = kept | ~in_candidate_block
+    return np.where(kept, role, 0).astype(np.int8)
 
 
 def bounds(offsets, seg) -> np.ndarray:

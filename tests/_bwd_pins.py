@@ -252,6 +252,77 @@ def pin_cand_only_dq_independent_of_history_gradient():
     assert np.max(np.abs(got[1] - full0[1][hr])) <= 1e-12 and np.max(np.abs(got[2] - full0[2][hr])) <= 1e-12
 
 
+def _fallback_layout_here(cb, q_hist_rows):
+    """The page's fallback layout of a candidate-only layer, built here row by row (not with
+    the oracle's helper): per user [frozen history | candidates] as one full-sequence user.
+    History rows get the queries ``q_hist_rows`` (their output gradient is zero, so these
+    must not matter).  Returns an object with the full-sequence fields and the row maps."""
+    from types import SimpleNamespace
+    hoff, coff = np.asarray(cb.hist_offsets), np.asarray(cb.cand_offsets)
+    q, k, v, rows_h, rows_c, offsets, cand_start = [], [], [], [], [], [0], []
+    for b in range(len(coff) - 1):
+        for j in range(int(hoff[b]), int(hoff[b + 1])):
+            rows_h.append(len(q))
+            q.append(q_hist_rows[j]); k.append(cb.k_hist[j]); v.append(cb.v_hist[j])
+        cand_start.append(len(q))
+        for j in range(int(coff[b]), int(coff[b + 1])):
+            rows_c.append(len(q))
+            q.append(cb.q_cand[j]); k.append(cb.k_cand[j]); v.append(cb.v_cand[j])
+        offsets.append(len(q))
+    shape = (0,) + tuple(np.shape(cb.q_cand)[1:])
+    arr = [np.asarray(x, np.float64).reshape((-1,) + shape[1:]) for x in (q, k, v)]
+    return SimpleNamespace(q=arr[0], k=arr[1], v=arr[2], offsets=np.asarray(offsets, np.int64),
+                           cand_start=np.asarray(cand_start, np.int64), valid=None,
+                           attend_padded_history=False, B=len(coff) - 1, H=shape[1], d=shape[2],
+                           hr=np.asarray(rows_h, np.int64), cr=np.asarray(rows_c, np.int64))
+
+
+def pin_cand_only_error_scale():
+    """``cand_only_gradient_error_scale`` (the tolerance scale of the five candidate-only
+    gradients) against:
+     * ``gradient_error_scale`` (pinned above) of the fallback layout built here, with a zero
+       output gradient on the history rows and random queries there, taken at the rows each
+       gradient belongs to;
+     * the triangle inequality against the candidate-only gradients (pinned by finite
+       differences);
+     * its equality case: with dO >= 0 every product of the history values' gradient has one
+       sign, so that scale equals the gradient;
+     * the error of candidate-only gradients computed with P, o and dS rounded to bfloat16."""
+    from workloads import make_cand_only_batch
+    rng = rng_for(98)
+    u = 2.0 ** -8
+    cb = make_cand_only_batch(rng, "co-err", hist=[4, 0, 3, 2], cand=[2, 3, 1, 0], H=2, d=6, dtype="f32",
+                              scaled=False)
+    ins = [np.asarray(x, np.float64) for x in (cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand)]
+    do = rng.standard_normal(cb.q_cand.shape)
+    es = G.cand_only_gradient_error_scale(*ins, do, cb.hist_offsets, cb.cand_offsets)
+    grads = G.cand_only_attention_backward(*ins, do, cb.hist_offsets, cb.cand_offsets)
+    fl = _fallback_layout_here(cb, rng.standard_normal((cb.Th,) + tuple(cb.q_cand.shape[1:])))
+    g_full = np.zeros(fl.q.shape)
+    g_full[fl.cr] = do
+    eq, ek, ev = G.gradient_error_scale(fl.q, fl.k, fl.v, g_full, fl.offsets, fl.cand_start)
+    want = (eq[fl.cr], ek[fl.hr], ev[fl.hr], ek[fl.cr], ev[fl.cr])
+    names = ("dq_cand", "dk_hist", "dv_hist", "dk_cand", "dv_cand")
+    for name, e, w, g in zip(names, es, want, grads):
+        assert e.shape == w.shape, name
+        assert np.max(np.abs(e - w), initial=0.0) <= 1e-12 * max(1.0, float(np.max(w, initial=0.0))), name
+        assert np.all(e >= np.abs(g) * (1 - 1e-12) - 1e-15), name          # triangle inequality
+    # history keys of the user without candidates (the last one) get a zero scale
+    last = slice(int(cb.hist_offsets[3]), int(cb.hist_offsets[4]))
+    assert np.all(es[1][last] == 0) and np.all(es[2][last] == 0)
+    # equality case for the history values' gradient
+    e_abs = G.cand_only_gradient_error_scale(*ins, np.abs(do), cb.hist_offsets, cb.cand_offsets)[2]
+    dv_abs = G.cand_only_attention_backward(*ins, np.abs(do), cb.hist_offsets, cb.cand_offsets)[2]
+    assert np.max(np.abs(e_abs - dv_abs)) <= 1e-12 * max(1.0, float(np.max(e_abs)))
+    # the scale bounds the error of the rounded computation, gradient by gradient
+    sc = 1.0 / math.sqrt(cb.d)
+    gr = _rounded_grads(fl, g_full, sc)
+    rounded = (gr[0][fl.cr], gr[1][fl.hr], gr[2][fl.hr], gr[1][fl.cr], gr[2][fl.cr])
+    for name, g, e, r in zip(names, grads, es, rounded):
+        assert np.all(np.abs(r - g) <= 1.02 * u * (e + np.abs(g)) + 1e-300), name
+
+
 BWD_PINS = [pin_finite_differences, pin_torch_autograd, pin_lse, pin_closed_forms,
             pin_isolation_of_gradients, pin_error_scale, pin_cand_only_finite_differences,
-            pin_cand_only_dq_independent_of_history_gradient]
+            pin_cand_only_dq_independent_of_history_gradient,
+            pin_cand_only_error_scale]

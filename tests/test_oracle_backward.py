@@ -47,3 +47,42 @@ def test_some_pin_catches(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutation {name}"
+
+
+def _cand_scale_factory(kind, real):
+    """Plausible mistakes in the candidate-only error scale: history key and value scales
+    exchanged, the candidates' own key and value scales exchanged, or the history and
+    candidate row maps of the fallback layout exchanged."""
+    def f(*args, **kw):
+        if kind == "rows_swapped":
+            orig = G._cand_only_as_full
+
+            def swapped(*a):
+                q, k, v, g, off, cs, hr, cr = orig(*a)
+                return q, k, v, g, off, cs, cr, hr
+            G._cand_only_as_full = swapped
+            try:
+                return real(*args, **kw)
+            finally:
+                G._cand_only_as_full = orig
+        eq, ekh, evh, ekc, evc = real(*args, **kw)
+        if kind == "hist_k_v_swapped":
+            return eq, evh, ekh, ekc, evc
+        return eq, ekh, evh, evc, ekc
+    return f
+
+
+CAND_SCALE_MUTATIONS = ["hist_k_v_swapped", "cand_k_v_swapped", "rows_swapped"]
+
+
+@pytest.mark.parametrize("name", CAND_SCALE_MUTATIONS)
+def test_some_pin_catches_cand_only_scale(name, monkeypatch):
+    monkeypatch.setattr(G, "cand_only_gradient_error_scale",
+                        _cand_scale_factory(name, G.cand_only_gradient_error_scale))
+    caught = []
+    for pin in _bwd_pins.BWD_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutation {name}"

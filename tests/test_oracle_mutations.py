@@ -13,29 +13,30 @@ from oracle import jagged as J
 
 
 def _mask_rows_factory(kind):
+    """Mistakes planted on top of the oracle's own mask rows."""
     orig = A.isolation_mask_rows
 
     def f(seg, rows):
         seg = np.asarray(seg)
         rows = np.asarray(rows, dtype=np.int64)
-        L = len(seg)
-        qh, qc = (seg == 1)[rows], (seg == -1)[rows]
-        kh, kc = seg == 1, seg == -1
-        same = rows[:, None] == np.arange(L)[None, :]
-        hist = kh[None, :] & (qh | qc)[:, None]
-        self_ = qc[:, None] & kc[None, :] & same
+        role = seg[rows]
+        out = orig(seg, rows).copy()
+        own = np.nonzero(role == -1)[0]
         if kind == "no_self":
-            return hist
-        if kind == "cands_see_cands":
-            return hist | (qc[:, None] & kc[None, :])
-        if kind == "history_sees_cands":
-            return hist | self_ | (qh[:, None] & kc[None, :])
-        if kind == "pad_query_attends":
-            return hist | self_ | ((seg == 0)[rows][:, None] & kh[None, :])
-        if kind == "self_shifted":
-            shifted = (rows[:, None] + 1) == np.arange(L)[None, :]
-            return hist | (qc[:, None] & kc[None, :] & shifted)
-        return orig(seg, rows)
+            out[own, rows[own]] = False
+        elif kind == "cands_see_cands":
+            out[np.ix_(role == -1, seg == -1)] = True
+        elif kind == "history_sees_cands":
+            out[np.ix_(role == 1, seg == -1)] = True
+        elif kind == "pad_query_attends":
+            out[np.ix_(role == 0, seg == 1)] = True
+        elif kind == "self_shifted":
+            out[own, rows[own]] = False
+            nxt = rows[own] + 1
+            keep = (nxt < len(seg))
+            keep[keep] = seg[nxt[keep]] == -1
+            out[own[keep], nxt[keep]] = True
+        return out
     return f
 
 
@@ -64,17 +65,19 @@ def _softmax_factory(kind):
 
 
 def _seg_factory(kind):
+    """Mistakes planted on top of the oracle's own segment rule."""
+    orig = J.segment_ids
+
     def f(offsets, cand_start, valid=None, attend_padded_history=False):
-        offsets = np.asarray(offsets, np.int64)
-        T = int(offsets[-1])
-        seg = np.zeros(T, np.int8)
-        for b in range(len(offsets) - 1):
-            for idx in range(int(offsets[b]), int(offsets[b + 1])):
-                isc = idx > cand_start[b] if kind == "strict_start" else idx >= cand_start[b]
-                ok = True if valid is None else bool(valid[idx])
-                if attend_padded_history and kind != "flag_ignored":
-                    ok = ok or (isc if kind == "flag_on_candidates" else not isc)
-                seg[idx] = (-1 if isc else 1) if ok else 0
+        if kind == "strict_start":       # the candidate block starts one row late
+            return orig(offsets, np.asarray(cand_start, np.int64) + 1, valid, attend_padded_history)
+        if kind == "flag_ignored":
+            return orig(offsets, cand_start, valid, False)
+        # flag_on_candidates: the flag revives padded candidates instead of padded history
+        seg = orig(offsets, cand_start, valid, False)
+        if attend_padded_history:
+            block = orig(offsets, cand_start, None, False) == -1
+            seg = np.where(block, np.int8(-1), seg).astype(np.int8)
         return seg
     return f
 
