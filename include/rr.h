@@ -56,7 +56,9 @@ typedef enum {
   RR_OK = 0,
   RR_EINVAL = -1,        /* NULL where not allowed, negative size, inconsistent sizes */
   RR_EDTYPE = -2,        /* dtype not RR_F32 / RR_BF16 */
-  RR_EUNSUPPORTED = -3,  /* d not in {16, 32, 64, 128}, or sizes past the documented limits */
+  RR_EUNSUPPORTED = -3,  /* d not in {16, 32, 64, 128}, or sizes past the documented limits
+                            (attention: H <= 1023 and fewer than 2^21 tiles of 64 query rows,
+                            i.e. at most 2^27 - 64 query rows per call) */
   RR_EWORKSPACE = -4,    /* workspace NULL or smaller than the *_workspace_bytes query */
   RR_EHIP = -5           /* a kernel launch failed */
 } rr_status;

@@ -34,6 +34,9 @@ int check_sizes(int32_t B, int32_t rows_kv, int32_t rows_q, int32_t H, int32_t d
   if (!supported_d(d)) return RR_EUNSUPPORTED;
   if (H > kMaxHeads) return RR_EUNSUPPORTED;
   if (item_upper_bound(B, rows_q, H) > 0x7fffffff) return RR_EUNSUPPORTED;
+  // a work item packs its query tile above the 10 head bits of an int32: tiles of the
+  // smallest height must number below 2^21 (about 134M query rows)
+  if ((static_cast<int64_t>(rows_q) + kBmMin - 1) / kBmMin >= kMaxTiles) return RR_EUNSUPPORTED;
   return RR_OK;
 }
 
@@ -71,7 +74,7 @@ const char* rr_status_string(int status) {
     case RR_OK: return "ok";
     case RR_EINVAL: return "invalid argument (NULL pointer, negative or inconsistent size)";
     case RR_EDTYPE: return "unsupported dtype (use RR_F32 or RR_BF16)";
-    case RR_EUNSUPPORTED: return "unsupported size (d must be 16, 32, 64 or 128; H <= 1023)";
+    case RR_EUNSUPPORTED: return "unsupported size (d must be 16, 32, 64 or 128; H <= 1023; rows < 2^27 - 63)";
     case RR_EWORKSPACE: return "workspace missing or too small";
     case RR_EHIP: return "HIP kernel launch failed";
     default: return "unknown status";

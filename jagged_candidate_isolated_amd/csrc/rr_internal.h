@@ -23,6 +23,7 @@ constexpr int kBmMin = 64;
 constexpr int kHeadSlots = 1024; // work items pack the head into 10 bits ...
 constexpr int kZeroHead = 1023;  // ... and head 1023 marks "zero these padding rows"
 constexpr int kMaxHeads = 1023;
+constexpr int64_t kMaxTiles = int64_t(1) << 21;   // ... and the query tile into the 21 bits above
 constexpr int kSortMax = 2048;   // users planned (and sorted) in LDS by the work-list builder
 
 // What one user contributes to an attention call.  Query and key lists are

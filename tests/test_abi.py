@@ -73,6 +73,23 @@ def test_attn_argument_errors():
     assert _attn(lib, T=0, q=None, ws=None) == rr.RR_OK
 
 
+def test_query_tile_index_limit():
+    """A work item packs its query tile above 10 head bits of an int32, so the library
+    refuses 2^21 or more 64-row query tiles (checked on the host; nothing is launched)."""
+    rr, lib = _lib()
+    last_ok = (1 << 27) - 64          # 2^21 - 1 tiles of 64 rows
+    first_bad = last_ok + 1
+    assert _attn(lib, B=1, T=first_bad, H=1) == rr.RR_EUNSUPPORTED
+    assert _attn(lib, B=1, T=(1 << 31) - 1, H=1) == rr.RR_EUNSUPPORTED
+    assert lib.rr_attn_workspace_bytes(1, first_bad, 1, 64) == 0
+    assert lib.rr_attn_workspace_bytes(1, last_ok, 1, 64) > 0
+    assert lib.rr_cand_only_workspace_bytes(1, 10, first_bad, 1, 128) == 0
+    assert lib.rr_cand_only_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 10, first_bad, 1, 128, 1,
+                                     0.0, FAKE, 1 << 40, None) == rr.RR_EUNSUPPORTED
+    # the key-major plan of the candidate-only backward tiles the frozen rows the same way
+    assert lib.rr_cand_only_bwd_workspace_bytes(1, first_bad, 10, 1, 128) == 0
+
+
 def test_cand_only_argument_errors():
     rr, lib = _lib()
     f = lib.rr_cand_only_attn_fwd
