@@ -188,3 +188,101 @@ def ranker_forward_cached(x_cand, cache, layers, hist_offsets, cand_offsets, H, 
     for layer, (kh, vh) in zip(layers, cache):
         x = block_cand_only(x, kh, vh, layer, hist_offsets, cand_offsets, H, d, base, scale)
     return x
+
+
+# --------------------------------------------------------------------------- rounding-error scale
+#
+# Not a result of the method: the spread that the probabilistic model of rounding errors
+# (each rounding multiplies its result by 1 + e, e independent and uniform in [-u, u])
+# gives each element of one layer's update (new state - old state) when the layer is
+# computed with h, q, k, v, the rotated q and k, the unnormalised attention weights before
+# the P v product and the attention output o rounded to bfloat16 (u = 2^-8), everything
+# else in float32.  The per-element standard deviation is estimated by running the layer
+# with such perturbations drawn from a seeded generator; a test bounds an implementation of
+# that arithmetic by a fixed multiple of it (plus float32-level terms, ``f32_slack``).
+
+U_BF16 = 2.0 ** -8
+U_F32 = 2.0 ** -24
+ROUNDING_POINTS = ("norm", "proj", "rotary", "weights", "output")
+
+
+def _perturbed_full_layer(x, layer, offsets, cand_start, H, d, base, scale, jitter):
+    """``block_full``'s update of x [T, D] with ``jitter(point, array)`` applied at each
+    rounding point; returns (update [T, D], attention output [T, H, d])."""
+    from .attention import _scale
+    x = np.asarray(x, np.float64)
+    D = H * d
+    h = jitter("norm", rms_norm(x, layer.gain))
+    qkv = jitter("proj", h @ np.asarray(layer.w_qkv, np.float64).T)
+    q, k, v = (qkv[:, i * D:(i + 1) * D].reshape(-1, H, d) for i in range(3))
+    pos = right_anchored_positions(offsets, cand_start)
+    qr, kr = jitter("rotary", rope(q, pos, base)), jitter("rotary", rope(k, pos, base))
+    sc = _scale(scale, d)
+    offsets = np.asarray(offsets, np.int64)
+    o = np.zeros_like(qr)
+    for b in range(len(offsets) - 1):
+        lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        # every row reads the rows before the candidate start; a candidate also itself
+        mask = np.zeros((n, n), dtype=bool)
+        mask[:, :cs - lo] = True
+        mask[np.arange(n), np.arange(n)] = True
+        for hh in range(H):
+            s = np.where(mask, sc * (qr[lo:hi, hh] @ kr[lo:hi, hh].T), -np.inf)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            o[lo:hi, hh] = jitter("output", (jitter("weights", w) @ v[lo:hi, hh]) / w.sum(axis=1, keepdims=True))
+    return o.reshape(len(x), D) @ np.asarray(layer.w_o, np.float64).T, o
+
+
+def full_layer_rounding_sigma(x, layer, offsets, cand_start, H, d, base=DEFAULT_BASE, scale=None,
+                              points=ROUNDING_POINTS, samples=128, seed=0):
+    """Per-element standard deviation [T, D] of ``block_full``'s update of x under the
+    probabilistic rounding model at ``points`` (a subset of ROUNDING_POINTS), estimated from
+    ``samples`` seeded draws."""
+    rng = np.random.default_rng(seed)
+    exact, _ = _perturbed_full_layer(x, layer, offsets, cand_start, H, d, base, scale, lambda p, a: a)
+
+    def jitter(point, a):
+        return a * (1.0 + rng.uniform(-U_BF16, U_BF16, a.shape)) if point in points else a
+    acc = np.zeros_like(exact)
+    for _ in range(samples):
+        upd, _ = _perturbed_full_layer(x, layer, offsets, cand_start, H, d, base, scale, jitter)
+        acc += (upd - exact) ** 2
+    return np.sqrt(acc / samples)
+
+
+def cand_only_layer_rounding_sigma(x_cand, x_hist, layer, hist_offsets, cand_offsets, H, d, base=DEFAULT_BASE,
+                                   scale=None, points=ROUNDING_POINTS, samples=128, seed=0):
+    """The same for a candidate-only layer's update of the candidates x_cand [Tc, D] over the
+    frozen rows x_hist (their keys and values carry the same roundings), computed on the
+    page's fallback layout: per user [frozen history | candidates], candidate rows kept."""
+    x, off, cs, rows = _fallback_layout(x_hist, x_cand, hist_offsets, cand_offsets)
+    return full_layer_rounding_sigma(x, layer, off, cs, H, d, base, scale, points, samples, seed)[rows]
+
+
+def f32_slack(x, layer, offsets, cand_start, H, d, base=DEFAULT_BASE, scale=None):
+    """Float32-level error terms of a layer's update [T, D]: the accumulation of o W_o^T over
+    D products, the residual add, and a few float32 roundings of every earlier step relative
+    to the update's magnitude."""
+    upd, o = _perturbed_full_layer(x, layer, offsets, cand_start, H, d, base, scale, lambda p, a: a)
+    wo = np.abs(np.asarray(layer.w_o, np.float64)).T
+    D = H * d
+    return (D + 2) * U_F32 * (np.abs(o.reshape(len(upd), D)) @ wo) + 4 * U_F32 * np.abs(np.asarray(x, np.float64)) \
+        + 2.0 ** -18 * np.abs(upd)
+
+
+def _fallback_layout(x_hist, x_cand, hist_offsets, cand_offsets):
+    """Per user [frozen history rows | candidate rows] as one full-sequence batch: (x, offsets,
+    cand_start, candidate rows)."""
+    hoff = np.asarray(hist_offsets, np.int64)
+    coff = np.asarray(cand_offsets, np.int64)
+    parts, off, cs, rows = [], [0], [], []
+    for b in range(len(coff) - 1):
+        parts += [np.asarray(x_hist, np.float64)[hoff[b]:hoff[b + 1]], np.asarray(x_cand, np.float64)[coff[b]:coff[b + 1]]]
+        cs.append(off[-1] + int(hoff[b + 1] - hoff[b]))
+        rows += range(cs[-1], cs[-1] + int(coff[b + 1] - coff[b]))
+        off.append(cs[-1] + int(coff[b + 1] - coff[b]))
+    x = np.concatenate(parts) if parts else np.zeros((0, np.shape(x_cand)[1]))
+    return x, np.asarray(off, np.int64), np.asarray(cs, np.int64), np.asarray(rows, np.int64)

@@ -190,4 +190,105 @@ def pin_invariants():
     assert np.array_equal(xc3[1:], xc[1:])
 
 
-RANKER_PINS = [pin_rms_norm, pin_torch_stack, pin_user_tokens, pin_closed_forms, pin_invariants]
+def _emulated_layer(x, L, offsets, cand_start, H, d, base, rounded):
+    """One full-sequence layer in float64 torch, written here, with bfloat16 rounding (torch's)
+    only at the points named in ``rounded``: "norm" (h), "proj" (q, k, v), "rotary" (the
+    rotated q and k), "weights" (the unnormalised softmax weights before the P v product;
+    their row sum stays exact) and "output" (the attention output).  Returns the new x."""
+    import torch
+    import torch.nn.functional as F
+    T, D = x.shape
+
+    def r(t, where):
+        return t.to(torch.bfloat16).to(torch.float64) if where in rounded else t
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    h = r(F.rms_norm(X, (D,), weight=torch.from_numpy(L.gain), eps=RK.RMS_EPS), "norm")
+    q, k, v = r(F.linear(h, torch.from_numpy(L.w_qkv)), "proj").split(D, dim=1)
+    pos = torch.zeros(T, dtype=torch.float64)
+    for b in range(len(cand_start)):
+        lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        for i in range(lo, hi):
+            pos[i] = min(i, cs) - lo
+    inv = base ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    rot = torch.polar(torch.ones(T, d // 2, dtype=torch.float64), pos[:, None] * inv[None, :])
+
+    def rotate(t):
+        c = torch.view_as_complex(t.reshape(T, H, d // 2, 2).contiguous())
+        return r(torch.view_as_real(c * rot[:, None, :]).reshape(T, H, d), "rotary")
+    q, k, v = rotate(q), rotate(k), v.reshape(T, H, d)
+    out = torch.zeros(T, H, d, dtype=torch.float64)
+    sc = 1.0 / np.sqrt(d)
+    for b in range(len(cand_start)):
+        lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        m = torch.tensor([[j < cs - lo or i == j for j in range(n)] for i in range(n)], dtype=torch.bool).reshape(n, n)
+        for hh in range(H):
+            s = (sc * q[lo:hi, hh] @ k[lo:hi, hh].T).masked_fill(~m, float("-inf"))
+            w = torch.exp(s - s.max(dim=1, keepdim=True).values)
+            out[lo:hi, hh] = r((r(w, "weights") @ v[lo:hi, hh]) / w.sum(dim=1, keepdim=True), "output")
+    return (X + F.linear(out.reshape(T, D), torch.from_numpy(L.w_o))).numpy()
+
+
+EMULATED = ("norm", "proj", "rotary", "weights", "output")
+
+
+def _fallback(x_hist, x_cand, hoff, coff):
+    """Per user [frozen history | candidates] as one full-sequence layout, and its candidate rows."""
+    rows, off, cs, cand_rows = [], [0], [], []
+    for b in range(len(coff) - 1):
+        rows += [x_hist[hoff[b]:hoff[b + 1]], x_cand[coff[b]:coff[b + 1]]]
+        cs.append(off[-1] + hoff[b + 1] - hoff[b])
+        cand_rows += list(range(cs[-1], cs[-1] + coff[b + 1] - coff[b]))
+        off.append(cs[-1] + coff[b + 1] - coff[b])
+    return np.concatenate(rows), np.asarray(off), np.asarray(cs), np.asarray(cand_rows, np.int64)
+
+
+def pin_layer_rounding_sigma():
+    """The rounding spread of one layer's update (``full_layer_rounding_sigma``,
+    ``cand_only_layer_rounding_sigma``) against deterministic round-to-nearest-even
+    emulations written here (torch's bfloat16 rounding): for each rounding point alone and
+    for all of them, the emulated update's error stays within 8 sigma of that point's
+    spread, element by element, and its root mean square over sigma lies in [0.1, 2] alone
+    and in [0.3, 1.2] for all points together (the
+    spread is neither too small nor vacuous; a dominant softmax weight of exactly 1 rounds
+    without error, which the model does not know, hence the low end).  Both layer kinds, a flat and a sharp
+    softmax.  W_o = 0 gives zero spread."""
+    base = 50.0
+    for sharp in (1.0, 4.0):
+        x, layers, off, cs, H, d = make_stack(61 + int(sharp), n_layers=1, H=2, d=8)
+        L = RK.Layer(layers[0].gain, layers[0].w_qkv * sharp, layers[0].w_o)
+        xh, xc, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+        kh, vh = RK.history_kv(xh, L, hoff, H, d, base)
+        fx, foff, fcs, frows = _fallback(xh, xc, hoff, coff)
+        cases = (
+            ("full", RK.block_full(x, L, off, cs, H, d, base),
+             lambda pts: RK.full_layer_rounding_sigma(x, L, off, cs, H, d, base, points=pts, samples=256),
+             lambda rnd: _emulated_layer(x, L, off, cs, H, d, base, rnd)),
+            ("cand-only", RK.block_cand_only(xc, kh, vh, L, hoff, coff, H, d, base),
+             lambda pts: RK.cand_only_layer_rounding_sigma(xc, xh, L, hoff, coff, H, d, base, points=pts,
+                                                           samples=256),
+             lambda rnd: _emulated_layer(fx, L, foff, fcs, H, d, base, rnd)[frows]),
+        )
+        # the model runs the layer itself: unperturbed, it is the oracle's layer
+        upd, _ = RK._perturbed_full_layer(x, L, off, cs, H, d, base, None, lambda p, a: a)
+        assert np.max(np.abs(x + upd - cases[0][1])) <= 1e-12
+        for kind, ref, sigma, emulate in cases:
+            for pts in [(p,) for p in EMULATED] + [EMULATED]:
+                sg = sigma(pts)
+                assert sg.shape == ref.shape and np.all(sg >= 0), (kind, pts)
+                err = np.abs(emulate(set(pts)) - ref)
+                live = sg > 0          # e.g. a lone candidate's output does not depend on its rotation
+                assert np.all(err[~live] <= 1e-14), (kind, pts)
+                z = err[live] / sg[live]
+                assert np.all(z <= 8.0), (kind, pts, sharp, float(z.max()))
+                rms = float(np.sqrt(np.mean(z * z)))
+                lo_rms, hi_rms = (0.3, 1.2) if len(pts) > 1 else (0.1, 2.0)
+                assert lo_rms <= rms <= hi_rms, (kind, pts, sharp, rms)
+    x, layers, off, cs, H, d = make_stack(65, n_layers=1, H=2, d=8)
+    L = RK.Layer(layers[0].gain, layers[0].w_qkv, np.zeros((H * d, H * d)))
+    assert np.all(RK.full_layer_rounding_sigma(x, L, off, cs, H, d, base, samples=4) == 0)
+
+RANKER_PINS = [pin_rms_norm, pin_torch_stack, pin_user_tokens, pin_closed_forms, pin_invariants,
+               pin_layer_rounding_sigma]

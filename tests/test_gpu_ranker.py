@@ -113,6 +113,28 @@ def test_rms_norm_bounds():
     assert np.all(np.abs(got - ref) <= (U + 2.0 ** -20) * np.abs(ref) + 1e-30)
 
 
+# Element by element: the layer's update against the oracle's, within 10 standard deviations
+# of the probabilistic rounding model at the bf16 rounding points of the layer (the oracle's
+# full_layer_rounding_sigma / cand_only_layer_rounding_sigma, 64 seeded draws: the estimate
+# is within about 25% of the true spread for almost every element) plus float32-level terms.
+SIGMA_K, SIGMA_SAMPLES = 10.0, 64
+
+
+def _elementwise(got, ref, base, sigma, slack, what):
+    err = np.abs((got - base) - (ref - base))
+    bound = SIGMA_K * sigma + slack
+    excess = err - bound
+    if np.max(excess) > 0:
+        i = np.unravel_index(int(np.argmax(excess / np.maximum(bound, 1e-300))), err.shape)
+        raise AssertionError(f"{what}: error {err[i]:.3e} over the bound {bound[i]:.3e} at {i} "
+                             f"(sigma {sigma[i]:.3e})")
+
+
+def _cand_only_slack(x_cand, x_hist, layer, hoff, coff, H, d):
+    x, off, cs, rows = RK._fallback_layout(x_hist, x_cand, hoff, coff)
+    return RK.f32_slack(x, layer, off, cs, H, d)[rows]
+
+
 def _frob(got, ref, base, what):
     """Relative Frobenius error of a layer's update (got - base against ref - base)."""
     e = np.linalg.norm(got - ref) / max(np.linalg.norm(ref - base), 1e-30)
@@ -125,7 +147,8 @@ def _frob(got, ref, base, what):
 @pytest.mark.parametrize("H,d", [(4, 32), (4, 64), (4, 128)])
 def test_each_layer_against_oracle(H, d):
     """The stack run with its first l layers, l = 1..L: layer l's update against the oracle's
-    layer applied to the GPU's state before it (no error carried between layers)."""
+    layer applied to the GPU's state before it (no error carried between layers), element by
+    element within the rounding model's spread and, as a second check, in Frobenius norm."""
     n_layers, n_cand_only = 4, 2
     x, off, cs, dl, ol = _setup(H, d, n_layers, seed=40 + d)
     xh0, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
@@ -137,6 +160,9 @@ def test_each_layer_against_oracle(H, d):
         if l <= n_full:
             got = _np(xd)
             ref = RK.block_full(prev_full, ol[l - 1], off, cs, H, d)
+            sg = RK.full_layer_rounding_sigma(prev_full, ol[l - 1], off, cs, H, d, samples=SIGMA_SAMPLES, seed=l)
+            _elementwise(got, ref, prev_full, sg, RK.f32_slack(prev_full, ol[l - 1], off, cs, H, d),
+                         f"full layer {l}")
             _frob(got, ref, prev_full, f"full layer {l}")
             prev_full = got
             prev_h, prev_c = RK.split_history_and_candidates(got, off, cs)[:2]
@@ -146,6 +172,10 @@ def test_each_layer_against_oracle(H, d):
             kh, vh = RK.history_kv(prev_h, ol[l - 1], hoff, H, d)
             ref = RK.block_cand_only(prev_c, kh, vh, ol[l - 1], hoff, coff, H, d)
             got = _np(xc)
+            sg = RK.cand_only_layer_rounding_sigma(prev_c, prev_h, ol[l - 1], hoff, coff, H, d,
+                                                   samples=SIGMA_SAMPLES, seed=l)
+            _elementwise(got, ref, prev_c, sg, _cand_only_slack(prev_c, prev_h, ol[l - 1], hoff, coff, H, d),
+                         f"candidate-only layer {l}")
             _frob(got, ref, prev_c, f"candidate-only layer {l}")
             prev_c = got
 
@@ -284,11 +314,26 @@ def test_user_token_attention():
     assert not got[qoff[1]:qoff[2]].any(), "a user with no keys must give 0"
 
 
+def _user_token_layout(cur_h, frozen_h, cur_c, is_p, p, hoff, coff):
+    """Per user [user tokens (current) | rest of the history (frozen) | candidates] as one
+    full-sequence batch, with the rows of the user tokens and of the candidates in it."""
+    parts, offs, cst, rows_p, rows_c = [], [0], [], [], []
+    for b in range(len(p)):
+        blk_h = np.where(is_p[hoff[b]:hoff[b + 1], None], cur_h[hoff[b]:hoff[b + 1]], frozen_h[hoff[b]:hoff[b + 1]])
+        parts += [blk_h, cur_c[coff[b]:coff[b + 1]]]
+        rows_p += range(offs[-1], offs[-1] + int(p[b]))
+        cst.append(offs[-1] + len(blk_h))
+        rows_c += range(cst[-1], cst[-1] + int(coff[b + 1] - coff[b]))
+        offs.append(cst[-1] + int(coff[b + 1] - coff[b]))
+    return np.concatenate(parts), np.asarray(offs), np.asarray(cst), np.asarray(rows_p), np.asarray(rows_c)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_user_token_layers_against_oracle(d):
     """candidate_only_layers_update_user_token: each candidate-only layer's update of the
-    user tokens and of the candidates against the oracle's layer on the GPU's own state;
-    the other rows before the candidate start stay frozen bit for bit."""
+    user tokens and of the candidates against the oracle's layer on the GPU's own state
+    (element by element within the rounding model's spread, and in Frobenius norm); the
+    other rows before the candidate start stay frozen bit for bit."""
     H, n_layers, n_cand_only = 4, 4, 2
     x, off, cs, dl, ol = _setup(H, d, n_layers, seed=90 + d)
     p = np.array(SHAPES["prefix"])
@@ -307,6 +352,12 @@ def test_user_token_layers_against_oracle(d):
         assert np.array_equal(got_h[~is_p], frozen_h[~is_p]), "a history row moved"
         ref_p, ref_c, _, _ = RK.block_user_token_layer(prev_h[is_p], frozen_h, prev_c, ol[l - 1], p, hoff, coff,
                                                        H, d, 10000.0, None)
+        # the layer is the full layer over each user's [user tokens | frozen history | candidates]
+        X, offs, cst, rows_p, rows_c = _user_token_layout(prev_h, frozen_h, prev_c, is_p, p, hoff, coff)
+        sg = RK.full_layer_rounding_sigma(X, ol[l - 1], offs, cst, H, d, samples=SIGMA_SAMPLES, seed=l)
+        sl = RK.f32_slack(X, ol[l - 1], offs, cst, H, d)
+        _elementwise(got_c, ref_c, prev_c, sg[rows_c], sl[rows_c], f"candidates, layer {l}")
+        _elementwise(got_h[is_p], ref_p, prev_h[is_p], sg[rows_p], sl[rows_p], f"user tokens, layer {l}")
         _frob(got_c, ref_c, prev_c, f"candidates, layer {l}")
         _frob(got_h[is_p], ref_p, prev_h[is_p], f"user tokens, layer {l}")
         prev_c, prev_h = got_c, got_h

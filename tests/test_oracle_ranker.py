@@ -55,3 +55,34 @@ def test_some_pin_catches(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutation {name}"
+
+
+def _sigma_mutation(kind):
+    real = RK.full_layer_rounding_sigma
+    real_layer = RK._perturbed_full_layer
+
+    def sigma(x, layer, offsets, cand_start, H, d, base=RK.DEFAULT_BASE, scale=None, points=RK.ROUNDING_POINTS,
+              samples=128, seed=0):
+        if kind == "rotary_point_dropped":
+            points = tuple(p for p in points if p != "rotary")
+        return real(x, layer, offsets, cand_start, H, d, base, scale, points, samples, seed)
+
+    def layer(x, L, offsets, cand_start, H, d, base, scale, jitter):
+        return real_layer(x, L, offsets, np.asarray(cand_start) + 1, H, d, base, scale, jitter)
+    return {"rotary_point_dropped": ("full_layer_rounding_sigma", sigma),
+            "late_candidate_start": ("_perturbed_full_layer", layer)}[kind]
+
+
+@pytest.mark.parametrize("name", ["u_halved", "u_doubled", "rotary_point_dropped", "late_candidate_start"])
+def test_rounding_sigma_mutations_caught(name, monkeypatch):
+    """Plausible mistakes in the layer's rounding spread: the unit roundoff off by a factor
+    2 either way, a rounding point left out, the layer's candidate start off by one."""
+    if name == "u_halved":
+        monkeypatch.setattr(RK, "U_BF16", 2.0 ** -9)
+    elif name == "u_doubled":
+        monkeypatch.setattr(RK, "U_BF16", 2.0 ** -7)
+    else:
+        attr, fn = _sigma_mutation(name)
+        monkeypatch.setattr(RK, attr, fn)
+    with pytest.raises(AssertionError):
+        _ranker_pins.pin_layer_rounding_sigma()
