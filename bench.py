@@ -48,9 +48,10 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default: about 1 s of work)")
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--config", type=int, default=2,
-                   help="2 short-history (default), 3 lognormal, 4 candidate-only, 5 skew, "
-                        "6 skew padded (attend_padded_history=True), 7 skew padded (False)")
+    p.add_argument("--config", type=int, default=None,
+                   help="2 short-history, 3 lognormal, 4 candidate-only, 5 skew (the default line, which "
+                        "also carries the short-history workload's roofline), 6 skew padded "
+                        "(attend_padded_history=True), 7 skew padded (False)")
     p.add_argument("--rope", action="store_true",
                    help="rotate q and k at right-anchored positions (rr_rope_qk) inside every step, "
                         "before the attention")
@@ -523,32 +524,49 @@ def ranker_cpu_baseline(b, x0, layers, budget_s, user_tokens=None):
             **host_info()}
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this path shards by "
-              "user with no exchange, and no multi-GPU figure is measured here.", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
-    from jagged_candidate_isolated_amd import rr
+SECONDARY_STEPS = 2000   # steps of the secondary (short-history) measurement of the default line
 
-    if args.calibrate_copy_mib:
-        calibrate_copy(args.calibrate_copy_mib)
-        return
-    cfg = args.config
+
+def timed_steps(torch, plan, run, steps, copies):
+    """Exactly ``steps`` steps (plan + run, step i on input copy i % copies), replayed from
+    captured HIP graphs so the host's launch overhead does not pace the GPU; bracketed by
+    device synchronisations.  Returns (seconds, timing mode)."""
+    n1 = min(steps, max(copies, 256))
+    reps, rem = divmod(steps, n1)
+
+    def capture(n, first):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(first, first + n):
+                plan(); run(i % copies)
+        g.replay()
+        return g
+    try:
+        g1 = capture(n1, 0)
+        g2 = capture(rem, reps * n1) if rem else None
+        torch.cuda.synchronize()
+    except Exception as e:  # pragma: no cover - depends on the runtime
+        print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            plan(); run(i % copies)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, "eager launches"
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g1.replay()
+    if g2 is not None:
+        g2.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, "hip graph replay"
+
+
+def measure(cfg, args, torch, rr, steps_req, warmup_req, with_cpu):
+    """One workload's bench record (the JSON object main prints)."""
+    import numpy as np
     b = make_batch(cfg)
-    if args.ranker:
-        if cfg in (4, 6, 7) or b.dtype != "bf16" or b.d not in (32, 64, 128) or (b.H * b.d) % 128:
-            print("--ranker runs the full-sequence bf16 workloads without padding (configs 2, 3, 5)",
-                  file=sys.stderr)
-            sys.exit(2)
-        run_ranker(args, b, torch, rr)
-        return
-    if args.backward and (b.dtype != "bf16" or b.d not in (64, 128) or args.rope):
-        print("--backward runs the bf16 workloads with d 64 or 128 (configs 2 to 7), without --rope",
-              file=sys.stderr)
-        sys.exit(2)
     eff_flops, exec_flops, alg_bytes, n_cands = work_counts(cfg, b)
     fwd_eff, fwd_exec = eff_flops, exec_flops
     if args.backward:       # a training step: forward + backward (2.5x the forward)
@@ -564,41 +582,16 @@ def main():
         plan(); run(i)
     torch.cuda.synchronize()
     est = (time.perf_counter() - t) / 3
-    steps = args.steps or int(min(5000, max(20, 1.0 / max(est, 1e-6))))
-    warmup = args.warmup if args.warmup is not None else max(5, steps // 10)
+    steps = steps_req or int(min(5000, max(20, 1.0 / max(est, 1e-6))))
+    warmup = warmup_req if warmup_req is not None else max(5, steps // 10)
 
     for i in range(warmup):
-        plan(); run(i)
+        plan(); run(i % copies)
     torch.cuda.synchronize()
 
-    # Timed region: the steps replay from a captured HIP graph (one plan + run per input
-    # copy), so the host's launch overhead does not pace the GPU.  Eager launches are the
-    # fallback if capture is unavailable.
-    graph = None
-    try:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(copies):
-                plan(); run(i)
-        graph.replay()
-        torch.cuda.synchronize()
-    except Exception as e:  # pragma: no cover - depends on the runtime
-        print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
-        graph = None
-    reps = max(1, math.ceil(steps / copies)) if graph is not None else steps
-    steps = reps * copies if graph is not None else steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(reps):
-        if graph is not None:
-            graph.replay()
-        else:
-            plan(); run(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, timing = timed_steps(torch, plan, run, steps, copies)
     ms_per_step = wall / steps * 1e3
     value = eff_flops / (ms_per_step / 1e3) / 1e12
-
     # One kernel alone: back-to-back launches replayed from a captured graph (no host
     # gaps), bracketed by HIP events recorded on the launch stream.
     stream = torch.cuda.current_stream()
@@ -675,7 +668,7 @@ def main():
         "effective_flops_per_step": eff_flops_all, "executed_flops_per_step": exec_flops_all,
         "executed_tflops": exec_flops_all / (ms_per_step / 1e3) / 1e12,
         "input_copies_rotated": copies, "footprint_bytes": footprint,
-        "timing": "hip graph replay" if graph is not None else "eager launches",
+        "timing": timing,
         "roofline": roof,
         # the forward kernel against both ceilings, whichever bounds it
         "fractions": {"mfma": (exec_flops / (kernel_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
@@ -703,8 +696,45 @@ def main():
                            "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
                            "alg_flops": bwd_flops}
         out["config"]["step"] = "plan + forward with lse + backward (dq, dk, dv)"
-    if not args.no_cpu_baseline:
+    if with_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, b, args.cpu_seconds, rope=args.rope, backward=args.backward)
+    return out
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this path shards by "
+              "user with no exchange, and no multi-GPU figure is measured here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from jagged_candidate_isolated_amd import rr
+
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+    default_line = args.config is None
+    cfg = 5 if default_line else args.config
+    args.config = cfg
+    if args.ranker:
+        b = make_batch(cfg)
+        if cfg in (4, 6, 7) or b.dtype != "bf16" or b.d not in (32, 64, 128) or (b.H * b.d) % 128:
+            print("--ranker runs the full-sequence bf16 workloads without padding (configs 2, 3, 5)",
+                  file=sys.stderr)
+            sys.exit(2)
+        run_ranker(args, b, torch, rr)
+        return
+    if args.backward and (cfg == 1 or args.rope):
+        print("--backward runs the bf16 workloads with d 64 or 128 (configs 2 to 7), without --rope",
+              file=sys.stderr)
+        sys.exit(2)
+    out = measure(cfg, args, torch, rr, args.steps, args.warmup, not args.no_cpu_baseline)
+    if default_line and not (args.rope or args.backward):
+        # the short-history workload's HBM roofline, measured in the same run
+        sec = measure(2, args, torch, rr, SECONDARY_STEPS, None, False)
+        out["secondary"] = {sec["config"]["workload"]: {
+            k: sec[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "candidates_per_s", "roofline",
+                                "fractions", "mfma_efficiency", "timing", "input_copies_rotated") if k in sec}}
     print(json.dumps(out), flush=True)
 
 
