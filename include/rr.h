@@ -131,6 +131,26 @@ int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int3
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * rr_attn_fwd_noalloc -- rr_attn_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace and allocates nothing (no hipMalloc, hipFree or allocating library
+ * call): the plan lives in a static device array of rr_attn_fwd_noalloc_max_bytes()
+ * bytes (16 MiB), one copy per GPU, held until the process ends.
+ *   arguments, layouts, ownership, stream semantics: as rr_attn_fwd (the caller passes
+ *     inputs and outputs; the current device must be the stream's device)
+ *   errors: as rr_attn_fwd; RR_EUNSUPPORTED when rr_attn_workspace_bytes(B, T, H, d)
+ *     exceeds rr_attn_fwd_noalloc_max_bytes(); RR_EHIP if the array's device address
+ *     cannot be looked up
+ *   concurrency: every call on a GPU shares that GPU's array; calls in stream order are
+ *     independent (each rewrites the whole plan), calls that overlap on one GPU race.
+ */
+size_t rr_attn_fwd_noalloc_max_bytes(void);
+int rr_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+                        const int32_t* cand_start, const uint8_t* valid, int attend_padded_history,
+                        int32_t B, int32_t T, int32_t H, int32_t d, int dtype, float scale,
+                        hipStream_t stream);
+
+/*
  * rr_attn_plan + rr_attn_run -- rr_attn_fwd in two steps.
  * The plan depends only on the batch's lengths (offsets, cand_start, valid, flag):
  * segment IDs and bounds per user, the compacted row lists when `valid` is given,

@@ -68,6 +68,9 @@ _SIGS = {
                                          ctypes.c_size_t, _P]),
     "rr_cand_only_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
                                         ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_attn_fwd_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "rr_attn_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int,
+                                           ctypes.c_float, _P]),
 }
 
 
@@ -209,6 +212,38 @@ def rr_attn_fwd(q, k, v, offsets, cand_start, valid=None, attend_padded_history=
         int(bool(attend_padded_history)), B, T, H, d, dt, float(scale or 0.0), _ptr(ws),
         ws.numel(), _stream(stream, dev)))
     return out
+
+
+def rr_attn_fwd_noalloc(q, k, v, offsets, cand_start, out, valid=None, attend_padded_history=False, scale=None,
+                        stream=None) -> torch.Tensor:
+    """rr_attn_fwd with no workspace: the library keeps the plan in a static device array
+    (rr_attn_fwd_noalloc_max_bytes() bytes per GPU) and allocates nothing; ``out`` is the
+    caller's output tensor [T, H, d] of q's dtype.  Calls that overlap on one GPU race."""
+    dev = q.device
+    _need(q, "q")
+    dt = _rr_dtype(q)
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        _need(t, name, q.dtype, dev)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d]")
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    if valid is not None:
+        _need(valid, "valid", torch.uint8, dev)
+    T, H, d = q.shape
+    B = offsets.numel() - 1
+    if cand_start.numel() != B:
+        raise ValueError("cand_start must have B entries")
+    _check("rr_attn_fwd_noalloc", _lib.rr_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(offsets), _ptr(cand_start), _ptr(valid),
+        int(bool(attend_padded_history)), B, T, H, d, dt, float(scale or 0.0), _stream(stream, dev)))
+    return out
+
+
+def rr_attn_fwd_noalloc_max_bytes() -> int:
+    return int(_lib.rr_attn_fwd_noalloc_max_bytes())
 
 
 def rr_cand_only_attn_fwd(q_cand, k_hist, v_hist, k_cand, v_cand, hist_offsets, cand_offsets,
