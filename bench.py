@@ -171,7 +171,7 @@ def self_planned(b) -> bool:
     if b.valid is not None or b.dtype != "bf16" or b.d < 32:
         return False
     bm = 256 if b.T >= 2048 * b.B else 128
-    q = 64
+    q = 8 * 32           # whole XCD chunks of the forward kernel
     grid = (b.H + 1) * ((b.T + bm - 1) // bm + b.B)
     grid = (grid + q - 1) // q * q
     return b.B <= 256 and b.B <= 2 * bm and grid <= 1024
@@ -226,12 +226,13 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
         hist_end, cand_first = hoff[1:].contiguous(), coff[:-1].contiguous()
 
         def plan():
-            rr.rr_cand_only_plan(hoff, coff, Th, Tc, H, d, dt, workspace=ws)
+            if not rope:      # the rotary step's attention call plans for itself
+                rr.rr_cand_only_plan(hoff, coff, Th, Tc, H, d, dt, workspace=ws)
 
-        def rope_only(i):
+        def rope_only(i):     # the keys' rotary pass (the queries turn inside the attention kernel)
             s = sets[i % copies]
             rr.rr_rope_qk(None, s[1], hoff, hist_end, k_out=rot[1])
-            rr.rr_rope_qk(s[0], s[3], coff, cand_first, pos_base=hist_len, q_out=rot[0], k_out=rot[3])
+            rr.rr_rope_qk(None, s[3], coff, cand_first, pos_base=hist_len, k_out=rot[3])
 
         def bwd_only(i):
             s = sets[i % copies]
@@ -241,7 +242,8 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
             s = sets[i % copies]
             if rope:
                 rope_only(i)
-                rr.rr_cand_only_run(rot[0], rot[1], s[2], rot[3], s[4], b.B, ws, out=outs[i % copies])
+                rr.rr_cand_only_attn_fwd_rope(s[0], rot[1], s[2], rot[3], s[4], hoff, coff, out=outs[i % copies],
+                                              workspace=ws)
             elif backward:
                 rr.rr_cand_only_run_lse(s[0], s[1], s[2], s[3], s[4], b.B, ws, out=outs[i % copies], lse=lse)
                 bwd_only(i)
@@ -258,12 +260,13 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
                            workspace=ws)
     else:
         def plan():
-            rr.rr_attn_plan(off, cst, b.T, b.H, b.d, dt, valid=valid,
-                            attend_padded_history=b.attend_padded_history, workspace=ws)
+            if not rope:      # the rotary step's attention call plans for itself
+                rr.rr_attn_plan(off, cst, b.T, b.H, b.d, dt, valid=valid,
+                                attend_padded_history=b.attend_padded_history, workspace=ws)
 
-        def rope_only(i):
+        def rope_only(i):     # the keys' rotary pass (the queries turn inside the attention kernel)
             s = sets[i % copies]
-            rr.rr_rope_qk(s[0], s[1], off, cst, q_out=rot[0], k_out=rot[1])
+            rr.rr_rope_qk(None, s[1], off, cst, k_out=rot[1])
 
         def bwd_only(i):
             s, g = sets[i % copies], grads[i % copies]
@@ -274,7 +277,7 @@ def gpu_setup(cfg, b, torch, rr, rope=False, backward=False):
             s = sets[i % copies]
             if rope:
                 rope_only(i)
-                rr.rr_attn_run(rot[0], rot[1], s[2], b.B, ws, out=outs[i % copies])
+                rr.rr_attn_fwd_rope(s[0], rot[1], s[2], off, cst, out=outs[i % copies], workspace=ws)
             elif backward:
                 rr.rr_attn_run_lse(s[0], s[1], s[2], b.B, ws, out=outs[i % copies], lse=lse)
                 bwd_only(i)
@@ -652,7 +655,7 @@ def measure(cfg, args, torch, rr, steps_req, warmup_req, with_cpu):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(b.name)
     roof["kernel"] = "k_attn_mfma" if b.dtype == "bf16" and b.d >= 32 else "k_attn_simple"
-    roof["self_planned"] = bool(cfg != 4 and self_planned(b) and not args.rope and not args.backward)
+    roof["self_planned"] = bool(cfg != 4 and self_planned(b) and not args.backward)
     roof["kernel_ms"] = kernel_ms
     if not (args.rope or args.backward):
         roof["kernel_ms_median"] = kernel_ms_median
@@ -682,13 +685,15 @@ def measure(cfg, args, torch, rr, steps_req, warmup_req, with_cpu):
                                   "mfma_tflops": mfma_flops / (kernel_ms / 1e3) / 1e12}
     if args.rope:
         es = 2 if b.dtype == "bf16" else 4
-        rows_qk = (b.Tc + b.Th + b.Tc) if cfg == 4 else 2 * b.T      # rows of q and k rotated
-        rope_bytes = 2 * rows_qk * b.H * b.d * es                     # each read once, written once
-        out["rope"] = {"kernel": "k_rope_qk", "kernel_ms": rope_ms, "bound": "hbm",
+        rows_k = (b.Th + b.Tc) if cfg == 4 else b.T                    # key rows rotated by the pass
+        rope_bytes = 2 * rows_k * b.H * b.d * es                      # each read once, written once
+        out["rope"] = {"kernel": "k_rope_qk (keys; queries rotate inside k_attn_mfma)", "kernel_ms": rope_ms,
+                       "bound": "hbm",
                        "achieved": rope_bytes / (rope_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": rope_bytes / (rope_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                        "alg_bytes": rope_bytes}
-        out["config"]["rope"] = "right-anchored rotary q/k, base 10000, inside every step"
+        out["config"]["rope"] = ("right-anchored rotary q/k, base 10000, inside every step: a rotary pass over the "
+                                 "keys, the queries rotated in registers by the attention kernel")
     if args.backward:
         bwd_flops = 2.5 * fwd_exec
         out["backward"] = {"kernels": ["k_bwd_dq", "k_bwd_dkdv"], "kernel_ms": bwd_ms, "bound": "mfma",
@@ -724,6 +729,10 @@ def main():
             sys.exit(2)
         run_ranker(args, b, torch, rr)
         return
+    if args.rope and cfg in (1, 6, 7):
+        print("--rope runs the unpadded bf16 workloads (configs 2 to 5): the queries turn inside the attention "
+              "kernel, which takes no padding mask", file=sys.stderr)
+        sys.exit(2)
     if args.backward and (cfg == 1 or args.rope):
         print("--backward runs the bf16 workloads with d 64 or 128 (configs 2 to 7), without --rope",
               file=sys.stderr)

@@ -131,6 +131,24 @@ int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int3
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * rr_attn_fwd_rope -- rr_attn_fwd with the queries' rotary encoding done inside the
+ * attention kernel (candidate isolation attention mask page, section
+ * "位置编码：候选共用一个位置": a history row sits at its place in the user's row, the
+ * newest at history_end - 1, and every candidate at history_end).  q is NOT rotated: the
+ * kernel rotates each query row in registers right after loading it, with the same angle
+ * and rotation arithmetic as rr_rope_qk, so the result equals, bit for bit, rr_attn_fwd
+ * on rr_rope_qk's rotated q.  k must already be rotated (rr_rope_qk with q = NULL), since
+ * every query tile of a user reads it; v is never rotated.
+ *   theta_base  rotary base (<= 0: 10000)
+ *   no padding mask (every row valid); bf16 with d in {32, 64, 128} only (else
+ *   RR_EUNSUPPORTED).  Other arguments, layouts, ownership, errors: as rr_attn_fwd.
+ */
+int rr_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+                     const int32_t* cand_start, int32_t B, int32_t T, int32_t H, int32_t d, int dtype,
+                     float scale, float theta_base, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
  * rr_attn_fwd_noalloc -- rr_attn_fwd for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
  * takes no workspace and allocates nothing (no hipMalloc, hipFree or allocating library
@@ -235,6 +253,22 @@ int rr_cand_only_attn_fwd(const void* q_cand, const void* k_hist, const void* v_
                           const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B,
                           int32_t Th, int32_t Tc, int32_t H, int32_t d, int dtype, float scale,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rr_cand_only_attn_fwd_rope -- rr_cand_only_attn_fwd with the candidates' rotary
+ * encoding done inside the attention kernel: every candidate of user b sits at position
+ * h_b = hist_offsets[b+1] - hist_offsets[b] (its frozen history's length, the history
+ * end).  q_cand is NOT rotated; k_hist (at positions 0 .. h_b - 1) and k_cand (at h_b)
+ * must already be rotated (rr_rope_qk).  Bit for bit equal to rr_cand_only_attn_fwd on
+ * rr_rope_qk's rotated q_cand.  bf16 with d in {32, 64, 128} only.  theta_base as
+ * rr_attn_fwd_rope; everything else as rr_cand_only_attn_fwd.
+ */
+int rr_cand_only_attn_fwd_rope(const void* q_cand, const void* k_hist, const void* v_hist,
+                               const void* k_cand, const void* v_cand, void* o_cand,
+                               const int32_t* hist_offsets, const int32_t* cand_offsets, int32_t B,
+                               int32_t Th, int32_t Tc, int32_t H, int32_t d, int dtype, float scale,
+                               float theta_base, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* rr_cand_only_attn_fwd in two steps, as rr_attn_plan / rr_attn_run (the frozen
  * history K/V of a user can be planned once and reused across candidate batches of

@@ -255,10 +255,16 @@ int rr_attn_bwd(const void* q, const void* k, const void* v, const void* o, cons
                          workspace_bytes, stream);
 }
 
-int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
-                const int32_t* cand_start, const uint8_t* valid, int attend_padded_history,
-                int32_t B, int32_t T, int32_t H, int32_t d, int dtype, float scale,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// rr_attn_fwd, with the queries rotated in the attention kernel when rope_log2_base != 0
+// (then the batch has no padding mask and the kernel is the MFMA one).
+int attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+             const int32_t* cand_start, const uint8_t* valid, int attend_padded_history, int32_t B, int32_t T,
+             int32_t H, int32_t d, int dtype, float scale, double rope_log2_base, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
   const int st = check_sizes(B, T, T, H, d, dtype);
   if (st != RR_OK) return st;
   if (B == 0 || T == 0 || H == 0) return RR_OK;
@@ -272,12 +278,41 @@ int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int3
     AttnArgs a = full_args(q, k, v, o, B, T, H, d, scale, workspace);
     a.offsets = offsets;
     a.cand_start = cand_start;
+    a.rope_log2_base = rope_log2_base;
     return status_of(launch_attn_mfma_self_planned(a, d, bm, grid, stream));
   }
   const int r = rr_attn_plan(offsets, cand_start, valid, attend_padded_history, B, T, H, d, dtype,
                              workspace, workspace_bytes, stream);
   if (r != RR_OK) return r;
-  return rr_attn_run(q, k, v, o, B, T, H, d, dtype, scale, workspace, workspace_bytes, stream);
+  AttnArgs a = full_args(q, k, v, o, B, T, H, d, scale, workspace);
+  a.rope_log2_base = rope_log2_base;
+  return run_attention(a, dtype, d, bm, T, stream);
+}
+
+double rope_log2(float theta_base) {
+  return log2((theta_base > 0.f && isfinite(theta_base)) ? static_cast<double>(theta_base) : 10000.0);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rr_attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+                const int32_t* cand_start, const uint8_t* valid, int attend_padded_history,
+                int32_t B, int32_t T, int32_t H, int32_t d, int dtype, float scale,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attn_fwd(q, k, v, o, offsets, cand_start, valid, attend_padded_history, B, T, H, d, dtype, scale, 0.0,
+                  workspace, workspace_bytes, stream);
+}
+
+int rr_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,
+                     const int32_t* cand_start, int32_t B, int32_t T, int32_t H, int32_t d, int dtype, float scale,
+                     float theta_base, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, T, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (!use_mfma(dtype, d)) return RR_EUNSUPPORTED;
+  return attn_fwd(q, k, v, o, offsets, cand_start, nullptr, 0, B, T, H, d, dtype, scale, rope_log2(theta_base),
+                  workspace, workspace_bytes, stream);
 }
 
 size_t rr_cand_only_workspace_bytes(int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d) {
@@ -321,6 +356,25 @@ int rr_cand_only_run(const void* q_cand, const void* k_hist, const void* v_hist,
   a.plan = p.header; a.meta = p.meta; a.idx = p.idx; a.items = p.items;
   a.B = B; a.H = H; a.mode = 1; a.rows = Tc;
   a.scale_log2 = softmax_scale_log2(scale, d);
+  return run_attention(a, dtype, d, tile_rows(dtype, d, B, Tc), Tc, stream);
+}
+
+int rr_cand_only_attn_fwd_rope(const void* q_cand, const void* k_hist, const void* v_hist, const void* k_cand,
+                               const void* v_cand, void* o_cand, const int32_t* hist_offsets,
+                               const int32_t* cand_offsets, int32_t B, int32_t Th, int32_t Tc, int32_t H, int32_t d,
+                               int dtype, float scale, float theta_base, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  const int st = check_sizes(B, Th, Tc, H, d, dtype);
+  if (st != RR_OK) return st;
+  if (!use_mfma(dtype, d)) return RR_EUNSUPPORTED;
+  if (B == 0 || Tc == 0 || H == 0) return RR_OK;
+  if (!q_cand || !k_cand || !v_cand || !o_cand) return RR_EINVAL;
+  if (Th > 0 && (!k_hist || !v_hist)) return RR_EINVAL;
+  const int r = rr_cand_only_plan(hist_offsets, cand_offsets, B, Th, Tc, H, d, dtype, workspace,
+                                  workspace_bytes, stream);
+  if (r != RR_OK) return r;
+  AttnArgs a = cand_args(q_cand, k_hist, v_hist, k_cand, v_cand, o_cand, B, Th, Tc, H, d, scale, workspace, 1);
+  a.rope_log2_base = rope_log2(theta_base);
   return run_attention(a, dtype, d, tile_rows(dtype, d, B, Tc), Tc, stream);
 }
 

@@ -39,7 +39,7 @@
 namespace rr {
 namespace {
 
-template <int D, int BN, int NW, int NS, bool KEY_IDX>
+template <int D, int BN, int NW, int NS, bool KEY_IDX, bool ROPE>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, const UserMeta& um,
                                           bool indexed, const Stages& st) {
   constexpr int kThreads = NW * 64;
@@ -76,7 +76,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(Qp + qrow * rs + 16 * kk + 8 * half);
-
   const int n_kv = um.n_kv;
   const int ntiles = (n_kv + BN - 1) / BN;
 
@@ -101,6 +100,35 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   }
   if constexpr (AHEAD > 2) {
     if (2 < ntiles) issue_tile(2, C2{});
+  }
+
+  if constexpr (ROPE) {
+    // Rotate this lane's query features in registers (the rotary pass's arithmetic, so the
+    // bits equal a query rotated by that pass): right-anchored positions -- a history row
+    // at its place in the user's row, every candidate at the history end n_kv.
+    // (after the first tiles' loads are issued, so that this work overlaps their latency)
+    for (int i = tid; i < D / 2; i += kThreads) st.inv_freq[i] = rotary_inv_freq(i, D, a.rope_log2_base);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's table writes done (lgkmcnt 0), loads may fly
+    tile_barrier();
+    const int pos = a.mode == 1 ? um.n_kv : min(min(qpos, um.n_q - 1), um.n_kv);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float c, s, y0, y1;
+        rotary_sincos(pos, st.inv_freq[8 * kk + 4 * half + j], c, s);
+        rotate_pair(static_cast<float>(qf[kk][2 * j]), static_cast<float>(qf[kk][2 * j + 1]), c, s, y0, y1);
+        qf[kk][2 * j] = static_cast<__bf16>(y0);
+        qf[kk][2 * j + 1] = static_cast<__bf16>(y1);
+      }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      // the rotated operand as opaque packed bf16: otherwise the compiler keeps the float
+      // rotations live through the key loop and packs them again at each use
+      v4i32 w = __builtin_bit_cast(v4i32, qf[kk]);
+      asm volatile("" : "+v"(w));
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   f32x16 oacc[DB];
@@ -286,37 +314,43 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   }
 }
 
-template <int D, int BN, int NW, int NS, bool SELF>
+template <int D, int BN, int NW, int NS, bool SELF, bool ROPE>
 __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   // pipeline stages (stages past NS are never referenced and take no LDS)
   __shared__ __attribute__((aligned(16))) u16 k0[BN * D], k1[BN * D], k2[BN * D], k3[BN * D];
   __shared__ __attribute__((aligned(16))) u16 v0[BN * D], v1[BN * D], v2[BN * D], v3[BN * D];
-  const Stages st{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
+  __shared__ double inv_freq[ROPE ? D / 2 : 1];
+  const Stages st{{k0, k1, k2, k3}, {v0, v1, v2, v3}, inv_freq};
   int2 it;
   UserMeta um;
   bool indexed = false;
   if constexpr (SELF) {   // an unpadded batch planned in this workgroup
     __shared__ SelfPlanLds sp;
-    if (!self_plan_item(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, xcd_item(blockIdx.x), sp, it, um))
+    if (!self_plan_item(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, xcd_item<kAttnXcdChunk>(blockIdx.x), sp, it, um))
       return;
-    attn_item<D, BN, NW, NS, false>(a, it, um, false, st);
+    attn_item<D, BN, NW, NS, false, ROPE>(a, it, um, false, st);
     return;
   }
-  if (!fetch_item(a, NW * kQw, xcd_item(blockIdx.x), it, um, indexed)) return;
+  if (!fetch_item(a, NW * kQw, xcd_item<kAttnXcdChunk>(blockIdx.x), it, um, indexed)) return;
   if (item_head(it) == kZeroHead) {
     zero_padding_tile(a, um, item_tile(it), NW * kQw, a.H * D * 2, threadIdx.x, NW * 64);
     return;
   }
   // key rows go through idx[] only for a padded user whose key rows are not one range
-  if (indexed && !um.kv_direct)
-    attn_item<D, BN, NW, NS, true>(a, it, um, indexed, st);
-  else
-    attn_item<D, BN, NW, NS, false>(a, it, um, indexed, st);
+  // (never with rotated queries: those calls take no padding mask)
+  if constexpr (!ROPE) {
+    if (indexed && !um.kv_direct) {
+      attn_item<D, BN, NW, NS, true, false>(a, it, um, indexed, st);
+      return;
+    }
+  }
+  attn_item<D, BN, NW, NS, false, ROPE>(a, it, um, indexed, st);
 }
 
 template <int D, int BN, int NW, int NS, bool SELF = false>
 hipError_t go(const AttnArgs& a, int64_t grid, hipStream_t s) {
-  return launch1(k_attn_mfma<D, BN, NW, NS, SELF>, grid, NW * 64, s, a);
+  if (a.rope_log2_base != 0.0) return launch1(k_attn_mfma<D, BN, NW, NS, SELF, true>, grid, NW * 64, s, a);
+  return launch1(k_attn_mfma<D, BN, NW, NS, SELF, false>, grid, NW * 64, s, a);
 }
 
 }  // namespace

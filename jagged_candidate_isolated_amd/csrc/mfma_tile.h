@@ -172,6 +172,7 @@ __device__ __forceinline__ void tile_barrier() {
 struct Stages {
   u16* k[4];
   u16* v[4];
+  double* inv_freq;   // the rotary inverse frequencies of the D/2 feature pairs (when rotating)
 };
 
 // Rows keep their running maximum as the softmax reference until a tile's maximum
@@ -285,15 +286,16 @@ __device__ __forceinline__ void wait_tiles(int later) {
 }
 
 // XCD-aware item order.  Workgroup i runs on XCD i % kXcds (the dispatcher deals
-// workgroups out round-robin), each XCD with its own L2.  Chunks of kXcdChunk
+// workgroups out round-robin), each XCD with its own L2.  Chunks of C
 // consecutive items -- query tiles of one user and head, which read the same keys
 // and values -- go to one XCD together, chunk c to XCD c % kXcds, so a K/V tile
 // comes into that L2 once and serves the whole chunk; chunks still start in the
-// work list's longest-first order.  The grid is a multiple of kXcds * kXcdChunk,
+// work list's longest-first order.  The grid is a multiple of kXcds * C,
 // which makes the map a permutation.
+template <int C = kXcdChunk>
 __device__ __forceinline__ int xcd_item(int wg) {
   const int x = wg % kXcds, slot = wg / kXcds;
-  return ((slot / kXcdChunk) * kXcds + x) * kXcdChunk + slot % kXcdChunk;
+  return ((slot / C) * kXcds + x) * C + slot % C;
 }
 
 }  // namespace

@@ -67,14 +67,6 @@ __global__ __launch_bounds__(256) void k_rope_positions(RopeArgs a, int32_t* pos
     pos[r] = position_of(a, static_cast<int>(r));
 }
 
-// sine and cosine of p * inv_freq: the product and its reduction modulo 2 pi in double
-__device__ __forceinline__ void rotary_sincos(int p, double inv_freq, float& c, float& s) {
-  const double x = static_cast<double>(p) * inv_freq;
-  const double two_pi = 6.283185307179586476925286766559;
-  const double r = x - two_pi * rint(x * (1.0 / two_pi));    // |r| <= pi
-  sincosf(static_cast<float>(r), &s, &c);
-}
-
 // 8 consecutive elements (4 pairs) as float
 __device__ __forceinline__ void load8(const float* p, float* x) {
   const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
@@ -140,10 +132,7 @@ __device__ __forceinline__ void rotate_heads(const T* x, T* y, int64_t first, in
       if (h0 + u < H) {
         float w[2 * NP];
 #pragma unroll
-        for (int j = 0; j < NP; ++j) {
-          w[2 * j] = fmaf(v[u][2 * j], c[j], -v[u][2 * j + 1] * s[j]);
-          w[2 * j + 1] = fmaf(v[u][2 * j], s[j], v[u][2 * j + 1] * c[j]);
-        }
+        for (int j = 0; j < NP; ++j) rotate_pair(v[u][2 * j], v[u][2 * j + 1], c[j], s[j], w[2 * j], w[2 * j + 1]);
         if constexpr (NP == 4) store8(y + first + static_cast<int64_t>(h0 + u) * d, w);
         else store2(y + first + static_cast<int64_t>(h0 + u) * d, w);
         if (y2) {
@@ -170,26 +159,56 @@ __device__ __forceinline__ void copy_heads(const T* x, T* y, int64_t first, int6
 
 // NP = 4: one thread per 4 consecutive pairs (d % 8 == 0); NP = 1 otherwise.  CACHE: also
 // fill the compact history blocks (a.kc, a.vc).
+constexpr int kRopeLdsUsers = 1024;   // batches up to this many users search their offsets in LDS
+constexpr int kRopeMaxD = 256;        // the largest head width the rotary pass takes
+
 template <typename T, int NP, bool CACHE>
 __global__ __launch_bounds__(256) void k_rope_qk(RopeArgs a) {
+  // the batch's offsets, candidate starts and position bases in LDS (one read per workgroup)
+  // so that each row's user is found without a chain of dependent global reads
+  __shared__ int32_t s_off[kRopeLdsUsers + 1], s_cs[kRopeLdsUsers], s_pb[kRopeLdsUsers];
+  __shared__ double s_inv[kRopeMaxD / 2];   // the pairs' inverse frequencies, once per workgroup
+  const bool in_lds = a.B <= kRopeLdsUsers;
+  if (in_lds) {
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) {
+      s_off[i] = a.offsets[i];
+      if (i < a.B) {
+        s_cs[i] = a.cand_start[i];
+        s_pb[i] = a.pos_base ? a.pos_base[i] : 0;
+      }
+    }
+  }
+  for (int i = threadIdx.x; i < a.d / 2; i += blockDim.x) s_inv[i] = rotary_inv_freq(i, a.d, a.log2_base);
+  __syncthreads();
   const int groups = a.d / (2 * NP);
   const int64_t n = static_cast<int64_t>(a.T) * groups;
   for (int64_t g = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; g < n;
        g += int64_t(gridDim.x) * blockDim.x) {
     const int r = static_cast<int>(g / groups), i0 = static_cast<int>(g % groups) * NP;
-    const int b = user_of(a.offsets, a.B, r);
-    const int off = a.offsets[b];
-    const int p = (a.pos_base ? a.pos_base[b] : 0) + min(r - off, a.cand_start[b] - off);
+    int b, off, cs, pb;
+    if (in_lds) {
+      int lo = 0, hi = a.B;   // the last b with offsets[b] <= r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      b = lo; off = s_off[b]; cs = s_cs[b]; pb = s_pb[b];
+    } else {
+      b = user_of(a.offsets, a.B, r);
+      off = a.offsets[b]; cs = a.cand_start[b]; pb = a.pos_base ? a.pos_base[b] : 0;
+    }
+    const int p = pb + min(r - off, cs - off);
     float c[NP], s[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j)
-      rotary_sincos(p, exp2(-(2.0 * (i0 + j) / a.d) * a.log2_base), c[j], s[j]);
+      rotary_sincos(p, s_inv[i0 + j], c[j], s[j]);
     const int64_t first = static_cast<int64_t>(r) * a.H * a.d + 2 * i0;
     if (a.q) rotate_heads<NP>(static_cast<const T*>(a.q), static_cast<T*>(a.qo), first, a.H, a.d, c, s);
     if constexpr (CACHE) {
       // a history row's place in the compact history blocks
       int64_t hrow = -1;
-      if (r < a.cand_start[b]) {
+      if (r < cs) {
         hrow = static_cast<int64_t>(a.hoff[b]) + r - off;
         if (hrow >= a.Th) hrow = -1;
       }

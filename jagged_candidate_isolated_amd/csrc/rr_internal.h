@@ -80,12 +80,20 @@ constexpr int kXcds = 8;
 #define RR_XCD_CHUNK 8
 #endif
 constexpr int kXcdChunk = RR_XCD_CHUNK;
+// The forward attention kernel keeps longer runs together: 32 consecutive items (query
+// tiles of one user and head) share an XCD, so a long user's keys and values enter
+// fewer L2s.
+#ifndef RR_ATTN_XCD_CHUNK
+#define RR_ATTN_XCD_CHUNK 32
+#endif
+constexpr int kAttnXcdChunk = RR_ATTN_XCD_CHUNK;
+static_assert(kAttnXcdChunk % kXcdChunk == 0, "attention chunks are whole backward chunks");
 
 // Workgroups of an attention launch for tile height bm: one per possible work item,
-// rounded up to whole XCD chunks.
+// rounded up to whole XCD chunks of the forward kernel (whole chunks of the backward too).
 inline int64_t attn_grid(int64_t B, int64_t rows, int64_t H, int bm) {
   const int64_t n = (H + 1) * ((rows + bm - 1) / bm + B);
-  const int64_t q = int64_t(kXcds) * kXcdChunk;
+  const int64_t q = int64_t(kXcds) * kAttnXcdChunk;
   return (n + q - 1) / q * q;
 }
 
@@ -130,6 +138,9 @@ struct AttnArgs {
   float* lse;          // [rows][H] natural-log sum of exp(scale q.k) over each row's keys, or NULL
   const int32_t* offsets;     // self-planned launches only: the batch's offsets and cand_start
   const int32_t* cand_start;
+  double rope_log2_base;      // != 0: rotate each query row in registers first (log2 of the base);
+                              // full sequence without padding: position min(row - start, n_kv),
+                              // candidate-only: position n_kv (the frozen history's length)
 };
 
 // The work item of workgroup slot `item` and its user: false when the plan in the
@@ -159,6 +170,50 @@ __device__ __forceinline__ int8_t segment_of(int row, int cand_start, const uint
   bool ok = valid ? (valid[row] != 0) : true;
   if (attend_padded_history) ok = ok || !is_candidate;
   return ok ? (is_candidate ? int8_t(-1) : int8_t(1)) : int8_t(0);
+}
+
+// Rotary encoding (candidate isolation mask page, section on positions shared by
+// candidates; the standard pairwise rotation).  The rotary pass and the attention
+// kernels that rotate their queries in registers share these, so a query rotated either
+// way has the same bits.
+// Inverse frequency of feature pair i of d: base^(-2i/d), in double.
+__device__ __forceinline__ double rotary_inv_freq(int i, int d, double log2_base) {
+  return exp2(-(2.0 * i / d) * log2_base);
+}
+// Sine and cosine of p * inv_freq.  The angle is formed and reduced in double (positions
+// reach 10^4 radians for the low frequencies, where a float angle would be off by about
+// 1e-3): a multiple k of pi/2 is taken off, leaving y in [-pi/4, pi/4]; sin y and cos y
+// are then the Taylor polynomials through y^9 and y^10 in float (their truncation error
+// at pi/4 is below 2e-9, under float precision), and the quadrant k mod 4 picks signs
+// and roles.  Short and branch-free, so a kernel that rotates its queries in registers
+// keeps its occupancy.
+__device__ __forceinline__ void rotary_sincos(int p, double inv_freq, float& c, float& s) {
+  const double x = static_cast<double>(p) * inv_freq;
+  const double half_pi = 1.5707963267948966192313216916398;
+  const double k = rint(x * (1.0 / half_pi));
+  const float y = static_cast<float>(fma(-k, half_pi, x));
+  const float y2 = y * y;
+  // sin y = y (1 - y^2/3! (1 - y^2/(4*5) (1 - y^2/(6*7) (1 - y^2/(8*9)))))
+  float ps = fmaf(-y2, 1.0f / 72.0f, 1.0f);
+  ps = fmaf(-y2 * (1.0f / 42.0f), ps, 1.0f);
+  ps = fmaf(-y2 * (1.0f / 20.0f), ps, 1.0f);
+  ps = fmaf(-y2 * (1.0f / 6.0f), ps, 1.0f);
+  const float sy = y * ps;
+  // cos y = 1 - y^2/2! (1 - y^2/(3*4) (1 - y^2/(5*6) (1 - y^2/(7*8) (1 - y^2/(9*10)))))
+  float pc = fmaf(-y2, 1.0f / 90.0f, 1.0f);
+  pc = fmaf(-y2 * (1.0f / 56.0f), pc, 1.0f);
+  pc = fmaf(-y2 * (1.0f / 30.0f), pc, 1.0f);
+  pc = fmaf(-y2 * (1.0f / 12.0f), pc, 1.0f);
+  const float cy = fmaf(-y2 * 0.5f, pc, 1.0f);
+  const int q = static_cast<int>(static_cast<long long>(k) & 3);
+  const float ss = (q & 1) ? cy : sy, cc = (q & 1) ? sy : cy;
+  s = (q & 2) ? -ss : ss;
+  c = ((q + 1) & 2) ? -cc : cc;
+}
+// one feature pair (x0, x1) turned by the angle whose cosine and sine are c, s
+__device__ __forceinline__ void rotate_pair(float x0, float x1, float c, float s, float& y0, float& y1) {
+  y0 = fmaf(x0, c, -x1 * s);
+  y1 = fmaf(x0, s, x1 * c);
 }
 
 constexpr int kBuckets = 128;      // logarithmic key-count buckets of the work list's sort

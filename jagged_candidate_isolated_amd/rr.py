@@ -68,6 +68,10 @@ _SIGS = {
                                          ctypes.c_size_t, _P]),
     "rr_cand_only_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
                                         ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_attn_fwd_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "rr_cand_only_attn_fwd_rope": (ctypes.c_int, [_P] * 8 + [_I, _I, _I, _I, _I, ctypes.c_int, ctypes.c_float,
+                                                             ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "rr_attn_fwd_noalloc_max_bytes": (ctypes.c_size_t, []),
     "rr_attn_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int,
                                            ctypes.c_float, _P]),
@@ -210,6 +214,70 @@ def rr_attn_fwd(q, k, v, offsets, cand_start, valid=None, attend_padded_history=
     _check("rr_attn_fwd", _lib.rr_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(offsets), _ptr(cand_start), _ptr(valid),
         int(bool(attend_padded_history)), B, T, H, d, dt, float(scale or 0.0), _ptr(ws),
+        ws.numel(), _stream(stream, dev)))
+    return out
+
+
+def rr_attn_fwd_rope(q, k, v, offsets, cand_start, theta_base=None, scale=None, out=None, workspace=None,
+                     stream=None) -> torch.Tensor:
+    """Full-sequence attention with the queries rotated inside the kernel: q unrotated, k
+    already rotated (rr_rope_qk with q=None); bf16, no padding mask."""
+    dev = q.device
+    _need(q, "q")
+    dt = _rr_dtype(q)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, q.dtype, dev)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d]")
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(cand_start, "cand_start", torch.int32, dev)
+    T, H, d = q.shape
+    B = offsets.numel() - 1
+    if cand_start.numel() != B:
+        raise ValueError("cand_start must have B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    ws = _workspace(rr_attn_workspace_bytes(B, T, H, d), workspace, dev)
+    _check("rr_attn_fwd_rope", _lib.rr_attn_fwd_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(offsets), _ptr(cand_start), B, T, H, d, dt,
+        float(scale or 0.0), float(theta_base or 0.0), _ptr(ws), ws.numel(), _stream(stream, dev)))
+    return out
+
+
+def rr_cand_only_attn_fwd_rope(q_cand, k_hist, v_hist, k_cand, v_cand, hist_offsets, cand_offsets,
+                               theta_base=None, scale=None, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Candidate-only attention with the candidates' queries rotated inside the kernel (at
+    their user's history length); k_hist and k_cand already rotated."""
+    dev = q_cand.device
+    _need(q_cand, "q_cand")
+    dt = _rr_dtype(q_cand)
+    Tc, H, d = q_cand.shape
+    for name, t in (("k_cand", k_cand), ("v_cand", v_cand)):
+        _need(t, name, q_cand.dtype, dev)
+        if t.shape != q_cand.shape:
+            raise ValueError(f"{name} must match q_cand")
+    for name, t in (("k_hist", k_hist), ("v_hist", v_hist)):
+        _need(t, name, q_cand.dtype, dev)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (H, d):
+            raise ValueError(f"{name} must be [Th, H, d]")
+    if k_hist.shape != v_hist.shape:
+        raise ValueError("k_hist and v_hist must have the same shape")
+    _need(hist_offsets, "hist_offsets", torch.int32, dev)
+    _need(cand_offsets, "cand_offsets", torch.int32, dev)
+    B = cand_offsets.numel() - 1
+    if hist_offsets.numel() != B + 1:
+        raise ValueError("hist_offsets and cand_offsets must both have B+1 entries")
+    Th = k_hist.shape[0]
+    if out is None:
+        out = torch.empty_like(q_cand)
+    _need(out, "out", q_cand.dtype, dev)
+    ws = _workspace(rr_cand_only_workspace_bytes(B, Th, Tc, H, d), workspace, dev)
+    _check("rr_cand_only_attn_fwd_rope", _lib.rr_cand_only_attn_fwd_rope(
+        _ptr(q_cand), _ptr(k_hist), _ptr(v_hist), _ptr(k_cand), _ptr(v_cand), _ptr(out), _ptr(hist_offsets),
+        _ptr(cand_offsets), B, Th, Tc, H, d, dt, float(scale or 0.0), float(theta_base or 0.0), _ptr(ws),
         ws.numel(), _stream(stream, dev)))
     return out
 

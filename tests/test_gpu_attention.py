@@ -360,7 +360,7 @@ def test_self_planned_random_batches(B):
     H = 2 if B <= 100 else 1
     fb = W.make_full_batch(rng, f"selfplan{B}", prefix=P, hist=h, cand=c, H=H, d=64, seed=9100 + B)
     # the library plans in-kernel for at most 256 users and a grid of at most 1024 workgroups
-    grid = -(-(H + 1) * (-(-fb.T // 128) + B) // 64) * 64
+    grid = -(-(H + 1) * (-(-fb.T // 128) + B) // 256) * 256
     assert fb.T < 2048 * B and grid <= 1024, "the batch must take the in-kernel planning path"
     dev = full_dev(fb)
     fused = run_full(fb, dev)

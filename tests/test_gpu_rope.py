@@ -133,3 +133,66 @@ def test_rope_cand_only_equals_full_rows():
     ref = R.cand_only_attention_rope(cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand,
                                      cb.hist_offsets, cb.cand_offsets)
     assert_close(co, ref, "bf16", "candidate-only layer with rotary q/k")
+
+
+# ---------------------------------------------------------------- queries rotated inside the attention
+
+
+@pytest.mark.parametrize("d,wide", [(32, False), (64, False), (128, False), (64, True), (128, True)])
+def test_fused_query_rotation_equals_the_rotary_pass(d, wide):
+    """rr_attn_fwd_rope (q rotated in the kernel's registers) gives the same bits as
+    rr_rope_qk followed by rr_attn_fwd, on the in-kernel-plan path and the separate plan,
+    narrow and wide tiles; and it matches the rotary oracle."""
+    rng = np.random.default_rng(600 + d + wide)
+    if wide:
+        fb = W.make_full_batch(rng, "rope-fused-wide", prefix=[3, 1], hist=[3000, 2200], cand=[1500, 2100], H=2, d=d,
+                               seed=610 + d)
+    else:
+        fb = W.make_full_batch(rng, "rope-fused", prefix=[4, 0, 2, 1], hist=[700, 0, 57, 260], cand=[33, 9, 0, 129],
+                               H=3, d=d, seed=620 + d)
+    assert (fb.T >= 2048 * fb.B) == wide
+    dv = full_dev(fb)
+    base = 500.0
+    _, k_rot = _rope_dev(None, dv["k"], dv["offsets"], dv["cand_start"], base=base)
+    q_rot, _ = _rope_dev(dv["q"], None, dv["offsets"], dv["cand_start"], base=base)
+    fused = rr().rr_attn_fwd_rope(dv["q"], k_rot, dv["v"], dv["offsets"], dv["cand_start"], theta_base=base)
+    two_pass = rr().rr_attn_fwd(q_rot, k_rot, dv["v"], dv["offsets"], dv["cand_start"])
+    ws = rr().rr_attn_plan(dv["offsets"], dv["cand_start"], fb.T, fb.H, fb.d, dv["q"].dtype)
+    planned = rr().rr_attn_run(q_rot, k_rot, dv["v"], fb.B, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two_pass), "fused rotation differs from the rotary pass"
+    assert torch.equal(fused, planned)
+    rows, heads = sample_full_rows(fb, 8, seed=d)
+    pos = R.right_anchored_positions(fb.offsets, fb.cand_start)
+    qr, kr = R.rope(fb.q, pos, base), R.rope(fb.k, pos, base)
+    ref = A.full_attention_rows(qr, kr, fb.v, fb.offsets, fb.cand_start, rows, heads)
+    assert_close(_np(fused)[rows, heads], ref, "bf16", "fused rotary attention")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_query_rotation_candidate_only(d):
+    """rr_cand_only_attn_fwd_rope: candidates rotated in the kernel at their user's history
+    length; equal bit for bit to rr_rope_qk + rr_cand_only_attn_fwd and to the fused
+    full-sequence layer's candidate rows."""
+    rng = np.random.default_rng(650 + d)
+    fb = W.make_full_batch(rng, "rope-fused-co", prefix=[2, 0, 1], hist=[400, 0, 90], cand=[64, 7, 130], H=2, d=d,
+                           seed=660 + d)
+    cb = W.split_to_cand_only(fb)
+    dc = cand_only_dev(cb)
+    hlen = (dc["hist_offsets"][1:] - dc["hist_offsets"][:-1]).contiguous()
+    _, kh = _rope_dev(None, dc["k_hist"], dc["hist_offsets"], dc["hist_offsets"][1:].contiguous())
+    qc, kc = _rope_dev(dc["q_cand"], dc["k_cand"], dc["cand_offsets"], dc["cand_offsets"][:-1].contiguous(),
+                       pos_base=hlen)
+    fused = rr().rr_cand_only_attn_fwd_rope(dc["q_cand"], kh, dc["v_hist"], kc, dc["v_cand"], dc["hist_offsets"],
+                                            dc["cand_offsets"])
+    two_pass = rr().rr_cand_only_attn_fwd(qc, kh, dc["v_hist"], kc, dc["v_cand"], dc["hist_offsets"],
+                                          dc["cand_offsets"])
+    dv = full_dev(fb)
+    _, k_rot = _rope_dev(None, dv["k"], dv["offsets"], dv["cand_start"])
+    full = rr().rr_attn_fwd_rope(dv["q"], k_rot, dv["v"], dv["offsets"], dv["cand_start"])
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two_pass)
+    assert torch.equal(fused, full[torch.from_numpy(cb.meta["cand_rows"]).to(full.device)])
+    ref = R.cand_only_attention_rope(cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand, cb.hist_offsets,
+                                     cb.cand_offsets)
+    assert_close(_np(fused), ref, "bf16", "fused rotary candidate-only attention")
