@@ -39,7 +39,15 @@
 namespace rr {
 namespace {
 
-template <int D, int BN, int NW, int NS, bool KEY_IDX, bool ROPE>
+// Early operand reads (the EAGER form of the tile loop, same arithmetic): for small
+// batches planned in the kernel, where one item's chain of key tiles sets the time
+// (short-history batch: 23.7 -> 22.3 us), and for d = 128 (1-2% faster on the skew and
+// candidate-only batches); at d = 64 in planned launches its extra registers cost a
+// wave per SIMD (lognormal batch 2% slower), so that form stays.
+template <int D, bool SELF>
+constexpr bool eager_reads() { return SELF || D == 128; }
+
+template <int D, int BN, int NW, int NS, bool KEY_IDX, bool ROPE, bool EAGER>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, const UserMeta& um,
                                           bool indexed, const Stages& st) {
   constexpr int kThreads = NW * 64;
@@ -245,9 +253,46 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     wait_tiles<LPT>(min(AHEAD - 1, ntiles - 1 - t));
     tile_barrier();
     if (t + AHEAD < ntiles) issue_tile(t + AHEAD, std::integral_constant<int, (CUR + AHEAD) % NS>{});
-    s_step(cur_tag);
-    softmax_step(t);
-    pv_step(cur_tag);
+    if constexpr (EAGER) {
+      // the same products with every LDS operand read issued early: all K operands before
+      // the S products, all V^T operands right after them, so that their latency passes
+      // during the products and the softmax instead of in front of each MFMA
+      const char* sk = reinterpret_cast<const char*>(st.k[CUR]);
+      const char* sv = reinterpret_cast<const char*>(st.v[CUR]);
+      bf16x8 kfs[KK][KB];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kfs[kk][kb] = *reinterpret_cast<const bf16x8*>(sk + k_off[kk] + kb * 32 * CH * 16);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfs[kk][kb], qf[kk], sacc[kb], 0, 0, 0);
+      bf16x8 vts[BN / 16][DB];
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vts[ks][db] = read_vt(sv + ks * 16 * CH * 16, v_off[db][0], v_off[db][1]);
+      softmax_step(t);
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks) {
+        const int kb = ks >> 1, s8 = (ks & 1) * 8;
+        bf16x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(sacc[kb][s8 + j]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vts[ks][db], pf, oacc[db], 0, 0, 0);
+      }
+    } else {
+      s_step(cur_tag);
+      softmax_step(t);
+      pv_step(cur_tag);
+    }
   };
   // One loop, NS tiles per trip, so that tile t always uses stage t % NS as a
   // compile-time constant; the tiles past the end of the list are skipped.
@@ -328,7 +373,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     __shared__ SelfPlanLds sp;
     if (!self_plan_item(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, xcd_item<kAttnXcdChunk>(blockIdx.x), sp, it, um))
       return;
-    attn_item<D, BN, NW, NS, false, ROPE>(a, it, um, false, st);
+    attn_item<D, BN, NW, NS, false, ROPE, eager_reads<D, true>()>(a, it, um, false, st);
     return;
   }
   if (!fetch_item(a, NW * kQw, xcd_item<kAttnXcdChunk>(blockIdx.x), it, um, indexed)) return;
@@ -340,11 +385,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   // (never with rotated queries: those calls take no padding mask)
   if constexpr (!ROPE) {
     if (indexed && !um.kv_direct) {
-      attn_item<D, BN, NW, NS, true, false>(a, it, um, indexed, st);
+      attn_item<D, BN, NW, NS, true, false, eager_reads<D, false>()>(a, it, um, indexed, st);
       return;
     }
   }
-  attn_item<D, BN, NW, NS, false, ROPE>(a, it, um, indexed, st);
+  attn_item<D, BN, NW, NS, false, ROPE, eager_reads<D, false>()>(a, it, um, indexed, st);
 }
 
 template <int D, int BN, int NW, int NS, bool SELF = false>
