@@ -101,12 +101,17 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   using C1 = std::integral_constant<int, 1 % NS>;
   using C2 = std::integral_constant<int, 2 % NS>;
   using C3 = std::integral_constant<int, 3 % NS>;
-  // prologue: the first AHEAD tiles in flight
+  // Four stages (the wide tile) take tiles in pairs: one barrier per two tiles, after
+  // which the next pair's loads go into the stages of the pair before.  (Per tile the
+  // eight waves wait at the barrier for the slowest; pairing halves those waits: the
+  // skew batch 0.7-1.3% faster.)  Same arithmetic either way.
+  constexpr bool PAIRS = NS == 4;
+  // prologue: the first tiles in flight (AHEAD, or one pair)
   if (0 < ntiles) issue_tile(0, C0{});
   if constexpr (AHEAD > 1) {
     if (1 < ntiles) issue_tile(1, C1{});
   }
-  if constexpr (AHEAD > 2) {
+  if constexpr (AHEAD > 2 && !PAIRS) {
     if (2 < ntiles) issue_tile(2, C2{});
   }
 
@@ -246,13 +251,25 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
 
   auto tile = [&](int t, auto cur_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
-    // Tile t has landed once no more than the loads of the tiles issued after it are
-    // outstanding (this wave's loads, retiring in order); the barrier makes every
-    // wave's loads visible and tells that every wave is done with the stage of tile
-    // t+AHEAD, refilled next to overlap the following tiles' math.
-    wait_tiles<LPT>(min(AHEAD - 1, ntiles - 1 - t));
-    tile_barrier();
-    if (t + AHEAD < ntiles) issue_tile(t + AHEAD, std::integral_constant<int, (CUR + AHEAD) % NS>{});
+    if constexpr (PAIRS) {
+      if constexpr (CUR % 2 == 0) {
+        // tiles t and t+1 have landed once none of this wave's loads is outstanding; past
+        // the barrier every wave's loads are visible and every wave is done with tiles
+        // t-2 and t-1, whose stages take t+2 and t+3
+        wait_vmem<0>();
+        tile_barrier();
+        if (t + 2 < ntiles) issue_tile(t + 2, std::integral_constant<int, (CUR + 2) % NS>{});
+        if (t + 3 < ntiles) issue_tile(t + 3, std::integral_constant<int, (CUR + 3) % NS>{});
+      }
+    } else {
+      // Tile t has landed once no more than the loads of the tiles issued after it are
+      // outstanding (this wave's loads, retiring in order); the barrier makes every
+      // wave's loads visible and tells that every wave is done with the stage of tile
+      // t+AHEAD, refilled next to overlap the following tiles' math.
+      wait_tiles<LPT>(min(AHEAD - 1, ntiles - 1 - t));
+      tile_barrier();
+      if (t + AHEAD < ntiles) issue_tile(t + AHEAD, std::integral_constant<int, (CUR + AHEAD) % NS>{});
+    }
     if constexpr (EAGER) {
       // the same products with every LDS operand read issued early: all K operands before
       // the S products, all V^T operands right after them, so that their latency passes
