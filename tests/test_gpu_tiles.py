@@ -78,6 +78,43 @@ def test_wide_equals_narrow_full_mode(d):
     assert_close(outs[0][rows, heads], ref, "bf16", "long user, sampled")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_wide_tile_short_key_lists(d):
+    """The wide tile takes key tiles in pairs (one barrier per two tiles): users whose key
+    lists end at and around tile boundaries (0 to 5 tiles of 64 keys, 0 to 3 of 128 at
+    d = 32) but with 2048 candidates each, so that the batch runs on 256-row tiles; the
+    same users followed by 300 tiny users run on 128-row tiles.  Bit-identical rows, and
+    sampled rows against the oracle."""
+    rng = np.random.default_rng(900 + d)
+    H = 2
+    nkv = np.array([0, 1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320, 321])
+    prefix = np.minimum(nkv, 3)
+    wide = W.make_full_batch(rng, "wide-short-keys", prefix=prefix, hist=nkv - prefix, cand=2048, H=H, d=d,
+                             seed=910 + d)
+    tiny = W.make_full_batch(rng, "tiny", prefix=rng.integers(0, 3, 300), hist=rng.integers(0, 5, 300),
+                             cand=rng.integers(1, 4, 300), H=H, d=d, seed=920 + d)
+    L = wide.T
+    mixed = W.make_full_batch(rng, "mixed", prefix=np.r_[wide.prefix, tiny.prefix], hist=np.r_[wide.hist, tiny.hist],
+                              cand=np.r_[wide.cand, tiny.cand], H=H, d=d, seed=930 + d)
+    mixed = W.FullBatch(**{**mixed.__dict__, "q": np.concatenate([wide.q, tiny.q]),
+                           "k": np.concatenate([wide.k, tiny.k]), "v": np.concatenate([wide.v, tiny.v])})
+    assert wide.T >= WIDE_ROWS * wide.B and mixed.T < WIDE_ROWS * mixed.B
+    _log(f"[tiles short keys] d={d} wide B={wide.B} T={wide.T} mixed B={mixed.B} T={mixed.T}")
+    dw, dm = full_dev(wide), full_dev(mixed)
+    outs = [run_full(wide, dw), _planned(wide, dw), run_full(mixed, dm)[:L], _planned(mixed, dm)[:L]]
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o, outs[0]), f"variant {i} differs from the wide-tile output"
+    # per user: its first and last key rows, its first two and last candidates
+    rows = []
+    for b in range(wide.B):
+        lo, cs, hi = int(wide.offsets[b]), int(wide.cand_start[b]), int(wide.offsets[b + 1])
+        rows += ([lo, cs - 1] if cs > lo else []) + [cs, cs + 1, hi - 1]
+    rows = np.array(rows)
+    heads = np.arange(len(rows)) % H
+    ref = A.full_attention_rows(wide.q, wide.k, wide.v, wide.offsets, wide.cand_start, rows, heads)
+    assert_close(outs[0][rows, heads], ref, "bf16", "short key lists on the wide tile, sampled")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_wide_equals_narrow_candidate_only(d):
     """A user with 2500 candidates over 1800 frozen rows: alone (wide tiles), inside a batch
