@@ -388,7 +388,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   bool indexed = false;
   if constexpr (SELF) {   // an unpadded batch planned in this workgroup
     __shared__ SelfPlanLds sp;
-    if (!self_plan_item(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, xcd_item<kAttnXcdChunk>(blockIdx.x), sp, it, um))
+    const int item = xcd_item<kAttnXcdChunk>(blockIdx.x);
+    // up to 64 users: every wave plans on its own, without LDS or barriers
+    if (!(a.B <= 64 ? self_plan_item_wave(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, item, it, um)
+                    : self_plan_item(a.offsets, a.cand_start, a.B, a.H, NW * kQw, a.rows, item, sp, it, um)))
       return;
     attn_item<D, BN, NW, NS, false, ROPE, eager_reads<D, true>()>(a, it, um, false, st);
     return;

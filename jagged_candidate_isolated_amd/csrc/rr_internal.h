@@ -337,6 +337,46 @@ __device__ __forceinline__ bool self_plan_item(const int32_t* offsets, const int
   return true;
 }
 
+// self_plan_item for a batch of at most 64 users, by every wave on its own (no LDS, no
+// barrier): lane u holds user u's counts; a user's place in the list (descending
+// key-count bucket, ties by user index: self_plan_item's order) and its first item, the
+// item count of the users before it, come from one pass over the 64 lanes.
+__device__ __forceinline__ bool self_plan_item_wave(const int32_t* offsets, const int32_t* cand_start, int B, int H,
+                                                    int bm, int rows, int item, int2& it, UserMeta& um) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, nq = 0, nkv = 0, key = (kBuckets << 6) | lane;   // past every user of the batch
+  if (lane < B) {   // row ranges clamped into [0, rows), as the planning kernel does
+    lo = min(max(offsets[lane], 0), rows);
+    const int hi = min(max(offsets[lane + 1], lo), rows);
+    const int cs = min(max(cand_start[lane], lo), hi);
+    nq = hi - lo;
+    nkv = cs - lo;
+    key = (cost_bucket(nkv) << 6) | lane;
+  }
+  const int cnt = H * ((nq + bm - 1) / bm);
+  int first = 0, total = 0;
+#pragma unroll 8
+  for (int v = 0; v < 64; ++v) {
+    const int kv = __builtin_amdgcn_readlane(key, v), cv = __builtin_amdgcn_readlane(cnt, v);
+    first += kv < key ? cv : 0;
+    total += cv;
+  }
+  if (item >= total) return false;
+  const uint64_t own = __ballot(cnt > 0 && first <= item && item < first + cnt);   // one lane
+  const int u = __ffsll(static_cast<long long>(own)) - 1;
+  const int nq_u = __builtin_amdgcn_readlane(nq, u), nkv_u = __builtin_amdgcn_readlane(nkv, u);
+  const int nqt = (nq_u + bm - 1) / bm, local = item - __builtin_amdgcn_readlane(first, u);
+  it = make_int2(u, ((local % nqt) << 10) | (local / nqt));
+  um = UserMeta{};
+  um.q_begin = __builtin_amdgcn_readlane(lo, u);
+  um.n_q = nq_u;
+  um.kv_begin = um.q_begin;
+  um.n_kv = nkv_u;
+  um.cand_rel = nkv_u;
+  um.kv_direct = 1;
+  return true;
+}
+
 // Launch a kernel that takes one parameter struct; returns the launch status
 // (hipLaunchKernel reports it directly, so no sticky last-error is read or cleared).
 template <typename P>

@@ -348,7 +348,7 @@ def test_self_planned_equals_planned(cfg):
         assert_close(fused, _oracle_full(fb), "bf16", f"self-planned {cfg}")
 
 
-@pytest.mark.parametrize("B", [1, 17, 100, 256])
+@pytest.mark.parametrize("B", [1, 17, 64, 65, 100, 256])
 def test_self_planned_random_batches(B):
     """In-kernel planning on random small batches (many users in one key-count bucket,
     empty users, users with no history): bit-identical to plan + run."""
