@@ -25,11 +25,13 @@
 // operand is read in that same permuted order so the A and B operands agree.
 //
 // Pipeline.  K and V tiles go to LDS by direct-to-LDS loads (no register staging)
-// into NS rotating buffers, NS-1 tiles ahead of the tile being computed; one
-// barrier per tile.  Two tile shapes: narrow (four waves, 128 query rows, two stages,
-// two to four workgroups per CU) and wide (eight waves, 256 query rows, four stages, one
+// into NS rotating buffers.  Two tile shapes: narrow (four waves, 128 query rows, two
+// stages, one tile ahead of the tile being computed and one barrier per tile, two to four
+// workgroups per CU) and wide (eight waves, 256 query rows, four stages taken in pairs:
+// one barrier per two tiles, the next pair loading while a pair is computed; one
 // workgroup per CU) for batches of long users.  A small unpadded batch can skip the
-// planning kernel: each workgroup then builds the work list itself (self_plan_item).
+// planning kernel: each workgroup then builds the work list itself (self_plan_item, or
+// self_plan_item_wave per wave for up to 64 users).
 //
 // Numerics: bf16 operands, fp32 accumulation, online softmax in fp32 with exp2
 // (scale * log2 e folded into one FMA), P rounded to bf16 for the PV product,
