@@ -399,6 +399,29 @@ def test_maximum_heads(d):
         rr().rr_attn_fwd(q, q, q, off, torch.tensor([2], dtype=torch.int32, device="cuda"))
 
 
+def test_user_keys_past_2_gib():
+    """One user whose key rows span more than 2 GiB (H = 1023, d = 128: 262 KB a row, 8304
+    keys), so its full key tiles leave the 32-bit buffer ranges for 64-bit addresses, and
+    a second user whose rows start past 2 GiB: sampled rows and heads against the oracle
+    (only those rows of the 2.2 GB output come back to the host)."""
+    from _gpu import rr
+    H, d = 1023, 128
+    fb = W.make_full_batch(np.random.default_rng(5), "keys-past-2gib", prefix=[4, 2], hist=[8300, 60],
+                           cand=[16, 9], H=H, d=d, seed=9500)
+    assert (int(fb.cand_start[0]) - int(fb.offsets[0])) * H * d * 2 > 2 ** 31
+    _log(f"[keys past 2 GiB] B={fb.B} T={fb.T} H={H} d={d}")
+    dev = full_dev(fb)
+    out = rr().rr_attn_fwd(dev["q"], dev["k"], dev["v"], dev["offsets"], dev["cand_start"])
+    lo2 = int(fb.offsets[1])
+    rows = np.array([0, 3, 4, 4150, 8303, 8304, 8312, 8319, lo2, lo2 + 61, fb.T - 1], dtype=np.int64)
+    heads = np.array([0, 1022, 511, 7, 1000, 300, 0, 1022, 5, 600, 1022], dtype=np.int64)
+    got = out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()].float().cpu().numpy()
+    del out, dev
+    torch.cuda.empty_cache()
+    ref = A.full_attention_rows(fb.q, fb.k, fb.v, fb.offsets, fb.cand_start, rows, heads)
+    assert_close(got.astype(np.float64), ref, "bf16", "keys past 2 GiB")
+
+
 def test_one_long_user():
     """A single user of 60,000 rows (one long key chain per query tile, offsets far past
     16 bits): sampled rows against the oracle, and candidates read only history + self."""
