@@ -328,21 +328,31 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   // both lane halves hold partial sums of the same query
   float l_tot = halves_sum(l_i);
 
-  // candidate self-term: <q, own k> as a dot product split across the two halves
-  float sd = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const uint4 kw = *reinterpret_cast<const uint4*>(KSp + qrow * rs + 16 * kk + 8 * half);
-    const unsigned kwv[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sd = fmaf(static_cast<float>(qf[kk][2 * j]), bf16_lo(kwv[j]), sd);
-      sd = fmaf(static_cast<float>(qf[kk][2 * j + 1]), bf16_hi(kwv[j]), sd);
-    }
-  }
-  sd = halves_sum(sd);
   float mref = m_i;   // the reference the row's sum l_tot is taken against (log2 units)
   if (qpos >= um.cand_rel) {
+    // candidate self-term: <q, own k> as a dot product split across the two halves (both
+    // halves of a query take this branch together).  The own key and value are loaded
+    // together, and only by candidates: a wave of history rows loads neither.
+    uint4 kw[KK];
+    uint2 vw[DB][4];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kw[kk] = *reinterpret_cast<const uint4*>(KSp + qrow * rs + 16 * kk + 8 * half);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        vw[db][g] = *reinterpret_cast<const uint2*>(VSp + qrow * rs + db * 32 + 8 * g + 4 * half);
+    float sd = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const unsigned kwv[4] = {kw[kk].x, kw[kk].y, kw[kk].z, kw[kk].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sd = fmaf(static_cast<float>(qf[kk][2 * j]), bf16_lo(kwv[j]), sd);
+        sd = fmaf(static_cast<float>(qf[kk][2 * j + 1]), bf16_hi(kwv[j]), sd);
+      }
+    }
+    sd = halves_sum(sd);
     const float ts = sd * sl2;
     const float mn = fmaxf(m_i, ts);
     mref = mn;
@@ -353,12 +363,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const uint2 vw =
-            *reinterpret_cast<const uint2*>(VSp + qrow * rs + db * 32 + 8 * g + 4 * half);
-        oacc[db][4 * g + 0] = oacc[db][4 * g + 0] * al + be * bf16_lo(vw.x);
-        oacc[db][4 * g + 1] = oacc[db][4 * g + 1] * al + be * bf16_hi(vw.x);
-        oacc[db][4 * g + 2] = oacc[db][4 * g + 2] * al + be * bf16_lo(vw.y);
-        oacc[db][4 * g + 3] = oacc[db][4 * g + 3] * al + be * bf16_hi(vw.y);
+        oacc[db][4 * g + 0] = oacc[db][4 * g + 0] * al + be * bf16_lo(vw[db][g].x);
+        oacc[db][4 * g + 1] = oacc[db][4 * g + 1] * al + be * bf16_hi(vw[db][g].x);
+        oacc[db][4 * g + 2] = oacc[db][4 * g + 2] * al + be * bf16_lo(vw[db][g].y);
+        oacc[db][4 * g + 3] = oacc[db][4 * g + 3] * al + be * bf16_hi(vw[db][g].y);
       }
   }
 
