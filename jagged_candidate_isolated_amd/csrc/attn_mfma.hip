@@ -156,12 +156,21 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   uint32_t k_off[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) k_off[kk] = (ql * CH + ((2 * kk + half) ^ swz<CH>(ql))) * 16;
+  // per-lane LDS byte addresses of the V^T operand reads in stage 0.  Another stage or k-step
+  // adds a constant, which the reads take in their 16-bit immediate offset field: with the
+  // stage's array address added at each read instead, the wide d = 128 tile (V stages above
+  // 64 KB of LDS) spent 11 address additions per key tile (the skew batch 2.6% slower).
   uint32_t v_off[DB][2];
+  const uint32_t v_base = lds_address(st.v[0]);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    v_off[db][0] = vt_offset<D>(db, 0, lane);
-    v_off[db][1] = vt_offset<D>(db, 1, lane);
+    v_off[db][0] = v_base + vt_offset<D>(db, 0, lane);
+    v_off[db][1] = v_base + vt_offset<D>(db, 1, lane);
   }
+  auto vt_at = [&](auto stage_tag, int ks, int db) {
+    const uint32_t delta = lds_address(st.v[decltype(stage_tag)::value]) - v_base + ks * 16 * CH * 16;
+    return read_vt_lds(v_off[db][0] + delta, v_off[db][1] + delta);
+  };
 
   // S^T = K Q^T for this wave's 32 queries; the KB accumulator chains interleave
   auto s_step = [&](auto stage_tag) {
@@ -196,9 +205,16 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     float mx[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      // At d = 128 a chain of v_max3 (two elements an instruction, 8 per 16): the empty asm
+      // keeps the compiler from rebalancing it into a tree with two-operand maxima (11 per
+      // 16).  At d <= 64, where one item's chain of key tiles sets the time of small batches,
+      // the compiler's shallower tree stays (the same maximum either way).
       float m = max3f(sacc[kb][0], sacc[kb][1], sacc[kb][2]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) m = max3f(m, sacc[kb][r], sacc[kb][r + 1]);
+      for (int r = 3; r < 15; r += 2) {
+        if constexpr (D == 128) asm volatile("" : "+v"(m));
+        m = max3f(m, sacc[kb][r], sacc[kb][r + 1]);
+      }
       mx[kb] = fmaxf(m, sacc[kb][15]);
     }
 #pragma unroll
@@ -235,7 +251,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   };
   // O^T += V^T P^T
   auto pv_step = [&](auto stage_tag) {
-    const char* sv = reinterpret_cast<const char*>(st.v[decltype(stage_tag)::value]);
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
       const int kb = ks >> 1, s8 = (ks & 1) * 8;
@@ -243,11 +258,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(sacc[kb][s8 + j]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const char* base = sv + ks * 16 * CH * 16;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_vt(base, v_off[db][0], v_off[db][1]),
-                                                           pf, oacc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_at(stage_tag, ks, db), pf, oacc[db], 0, 0, 0);
     }
   };
 
@@ -277,7 +289,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
       // the S products, all V^T operands right after them, so that their latency passes
       // during the products and the softmax instead of in front of each MFMA
       const char* sk = reinterpret_cast<const char*>(st.k[CUR]);
-      const char* sv = reinterpret_cast<const char*>(st.v[CUR]);
       bf16x8 kfs[KK][KB];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
@@ -295,7 +306,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vts[ks][db] = read_vt(sv + ks * 16 * CH * 16, v_off[db][0], v_off[db][1]);
+        for (int db = 0; db < DB; ++db) vts[ks][db] = vt_at(cur_tag, ks, db);
       softmax_step(t);
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {

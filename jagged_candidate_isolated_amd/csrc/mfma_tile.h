@@ -57,6 +57,14 @@ __device__ __forceinline__ uint32_t vt_offset(int db, int part, int lane) {
   return static_cast<uint32_t>((row * CH + (c ^ swz<CH>(row))) * 16 + sub);
 }
 
+// the same read at two LDS byte addresses
+__device__ __forceinline__ bf16x8 read_vt_lds(uint32_t a0, uint32_t a1) {
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(uintptr_t)a0);
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(uintptr_t)a1);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 w = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
 __device__ __forceinline__ bf16x8 read_vt(const char* sv, uint32_t off0, uint32_t off1) {
   const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(sv + off0));
   const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(sv + off1));
