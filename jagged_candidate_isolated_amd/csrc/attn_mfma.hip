@@ -159,7 +159,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   // per-lane LDS byte addresses of the V^T operand reads in stage 0.  Another stage or k-step
   // adds a constant, which the reads take in their 16-bit immediate offset field: with the
   // stage's array address added at each read instead, the wide d = 128 tile (V stages above
-  // 64 KB of LDS) spent 11 address additions per key tile (the skew batch 2.6% slower).
+  // 64 KB of LDS) spent 11 address additions per key tile.
   uint32_t v_off[DB][2];
   const uint32_t v_base = lds_address(st.v[0]);
 #pragma unroll
