@@ -213,17 +213,32 @@ __device__ __forceinline__ void dq_item(const BwdArgs& g, int h, int qt, const U
     if (t + 1 < ntiles) tile(t + 1, C1{});
   }
 
+  // The row's addresses again from an opaque copy of its index: otherwise the compiler
+  // forms them before the key loop and keeps them (in scratch, at d = 128) until here.
+  int qrow_e = qrow;
+  asm volatile("" : "+v"(qrow_e));
+  const int64_t ebase = static_cast<int64_t>(qrow_e) * rs;
   // a candidate reads its own key too: its term of dq, and the only gradient its own
   // key and value receive
   u16* dqp = static_cast<u16*>(g.dq) + h * D;
   if (qpos >= um.cand_rel) {
     const u16* KSp = static_cast<const u16*>(a.k_self) + h * D;
     const u16* VSp = static_cast<const u16*>(a.v_self) + h * D;
+    // q and dO as opaque copies too, so that their float forms from before the loop (the
+    // delta dot product) are not kept for these products
+    bf16x8 qe[KK], de[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      v4i32 wq = __builtin_bit_cast(v4i32, qf[kk]), wd = __builtin_bit_cast(v4i32, df[kk]);
+      asm volatile("" : "+v"(wq), "+v"(wd));
+      qe[kk] = __builtin_bit_cast(bf16x8, wq);
+      de[kk] = __builtin_bit_cast(bf16x8, wd);
+    }
     float sraw = 0.f, dp = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      sraw = dot8(qf[kk], load8(KSp + rbase + 16 * kk + 8 * half), sraw);
-      dp = dot8(df[kk], load8(VSp + rbase + 16 * kk + 8 * half), dp);
+      sraw = dot8(qe[kk], load8(KSp + ebase + 16 * kk + 8 * half), sraw);
+      dp = dot8(de[kk], load8(VSp + ebase + 16 * kk + 8 * half), dp);
     }
     const float p = __builtin_amdgcn_exp2f(fmaf(halves_sum(sraw), sl2, -lse2));
     const float ds = p * (halves_sum(dp) - drow);
@@ -231,23 +246,23 @@ __device__ __forceinline__ void dq_item(const BwdArgs& g, int h, int qt, const U
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
-        const uint2 kw = *reinterpret_cast<const uint2*>(KSp + rbase + db * 32 + 8 * gg + 4 * half);
+        const uint2 kw = *reinterpret_cast<const uint2*>(KSp + ebase + db * 32 + 8 * gg + 4 * half);
         dqacc[db][4 * gg + 0] = fmaf(ds, bf16_lo(kw.x), dqacc[db][4 * gg + 0]);
         dqacc[db][4 * gg + 1] = fmaf(ds, bf16_hi(kw.x), dqacc[db][4 * gg + 1]);
         dqacc[db][4 * gg + 2] = fmaf(ds, bf16_lo(kw.y), dqacc[db][4 * gg + 2]);
         dqacc[db][4 * gg + 3] = fmaf(ds, bf16_hi(kw.y), dqacc[db][4 * gg + 3]);
       }
     if (qvalid) {
-      u16* dkp = static_cast<u16*>(g.dk_self) + h * D + rbase;
-      u16* dvp = static_cast<u16*>(g.dv_self) + h * D + rbase;
+      u16* dkp = static_cast<u16*>(g.dk_self) + h * D + ebase;
+      u16* dvp = static_cast<u16*>(g.dv_self) + h * D + ebase;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        store8(dkp + 16 * kk + 8 * half, qf[kk], g.scale * ds);   // dk_c = scale ds q_c
-        store8(dvp + 16 * kk + 8 * half, df[kk], p);              // dv_c = p dO_c
+        store8(dkp + 16 * kk + 8 * half, qe[kk], g.scale * ds);   // dk_c = scale ds q_c
+        store8(dvp + 16 * kk + 8 * half, de[kk], p);              // dv_c = p dO_c
       }
     }
   }
-  if (qvalid) store_acc_row<DB>(dqp + rbase, dqacc, g.scale, half);
+  if (qvalid) store_acc_row<DB>(dqp + ebase, dqacc, g.scale, half);
 }
 
 template <int D, int BN>
@@ -429,8 +444,12 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& g, int h, int kt, const
     if (t + 1 < nqt) tile(t + 1, C1{});
   }
   if (kvalid) {
-    store_acc_row<DB>(static_cast<u16*>(g.dk) + h * D + kbase, dkacc, g.scale, half);
-    store_acc_row<DB>(static_cast<u16*>(g.dv) + h * D + kbase, dvacc, 1.f, half);
+    // the row's address again from an opaque copy of its index (not kept through the loop)
+    int krow_e = krow;
+    asm volatile("" : "+v"(krow_e));
+    const int64_t ebase = static_cast<int64_t>(krow_e) * rs;
+    store_acc_row<DB>(static_cast<u16*>(g.dk) + h * D + ebase, dkacc, g.scale, half);
+    store_acc_row<DB>(static_cast<u16*>(g.dv) + h * D + ebase, dvacc, 1.f, half);
   }
 }
 
