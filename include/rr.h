@@ -177,13 +177,19 @@ int rr_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, co
  * workspace, so a stack of layers over one batch can plan once and run per layer.
  * rr_attn_run must get the same B, T, H, d and dtype as the plan it uses; the
  * kernels check this against the plan and leave `o` unwritten if they differ.
- * A plan stays valid until the workspace is overwritten.
+ * A plan stays valid until the workspace is overwritten.  rr_attn_run leaves the plan
+ * as it is but writes another area of the workspace: for batches of long users (the
+ * 256-row query tile) a pass over k first stores, per 64 key rows and head, the largest
+ * squared key norm, from which the attention kernel bounds every row's scores
+ * (Cauchy-Schwarz) and skips forming tile maxima that cannot change its softmax
+ * reference; the output bits are the same either way.  Runs over one workspace must
+ * therefore be ordered on one stream: concurrent runs over a shared workspace race.
  */
 int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_t* valid,
                  int attend_padded_history, int32_t B, int32_t T, int32_t H, int32_t d, int dtype,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T, int32_t H,
-                int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                int32_t d, int dtype, float scale, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
 /*
@@ -193,7 +199,7 @@ int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B,
  *      pass recomputes the softmax from it.  NULL = not written (then as rr_attn_run).
  */
 int rr_attn_run_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                    int32_t T, int32_t H, int32_t d, int dtype, float scale, const void* workspace,
+                    int32_t T, int32_t H, int32_t d, int dtype, float scale, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -65,6 +65,21 @@ int run_attention(const AttnArgs& a, int dtype, int d, int bm, int64_t rows, hip
   return status_of(e);
 }
 
+// A full-sequence run over the plan in `workspace`.  With the wide tile (long users, many
+// key tiles per query tile) the key-norm pass first writes its bounds into the workspace,
+// so that the attention kernel can skip forming tile maxima that cannot move a row's
+// reference (same bits either way; the pass reads the key rows once).
+int run_full(AttnArgs a, int dtype, int d, int bm, int32_t T, void* workspace, hipStream_t stream) {
+  if (use_mfma(dtype, d) && bm == kBmMfmaWide) {
+    const WsLayout w = ws_layout(a.B, T, T, a.H);
+    a.knorm = carve<float>(workspace, w.knorm);
+    a.knorm_tiles = static_cast<int32_t>(w.knorm_tiles);
+    const hipError_t e = launch_key_norms(a, T, d, stream);
+    if (e != hipSuccess) return status_of(e);
+  }
+  return run_attention(a, dtype, d, bm, T, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,14 +210,14 @@ int rr_attn_plan(const int32_t* offsets, const int32_t* cand_start, const uint8_
 }
 
 int rr_attn_run(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t T, int32_t H,
-                int32_t d, int dtype, float scale, const void* workspace, size_t workspace_bytes,
+                int32_t d, int dtype, float scale, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
   return rr_attn_run_lse(q, k, v, o, nullptr, B, T, H, d, dtype, scale, workspace, workspace_bytes,
                          stream);
 }
 
 int rr_attn_run_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                    int32_t T, int32_t H, int32_t d, int dtype, float scale, const void* workspace,
+                    int32_t T, int32_t H, int32_t d, int dtype, float scale, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   const int st = check_sizes(B, T, T, H, d, dtype);
   if (st != RR_OK) return st;
@@ -211,7 +226,7 @@ int rr_attn_run_lse(const void* q, const void* k, const void* v, void* o, float*
   if (!workspace || workspace_bytes < ws_layout(B, T, T, H).total) return RR_EWORKSPACE;
   AttnArgs a = full_args(q, k, v, o, B, T, H, d, scale, workspace);
   a.lse = lse;
-  return run_attention(a, dtype, d, tile_rows(dtype, d, B, T), T, stream);
+  return run_full(a, dtype, d, tile_rows(dtype, d, B, T), T, workspace, stream);
 }
 
 size_t rr_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d) {
@@ -286,7 +301,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t
   if (r != RR_OK) return r;
   AttnArgs a = full_args(q, k, v, o, B, T, H, d, scale, workspace);
   a.rope_log2_base = rope_log2_base;
-  return run_attention(a, dtype, d, bm, T, stream);
+  return run_full(a, dtype, d, bm, T, workspace, stream);
 }
 
 double rope_log2(float theta_base) {

@@ -146,6 +146,42 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     }
   }
 
+  // A bound on this row's scaled scores against every key of the user, |q| max|k| (the
+  // key-norm pass gives max|k|^2 per 64 key rows and head), or +inf without one.  Once
+  // every row of the wave has its reference within kLazyRescale of its bound, no later
+  // tile can move a reference, and the tiles skip forming their maximum: the decision
+  // the maximum would give, so the same bits.  (Read after the first tiles' loads are
+  // issued: the wait for these loads falls where the first tile waits anyway.)
+  // (Wide tiles only: the host runs the key-norm pass for them alone, and in the narrow
+  // kernels the second loop below costs registers -- at d = 64 a wave per SIMD.)
+  constexpr bool BOUNDED = NW * kQw == kBmMfmaWide;
+  float qbound = INFINITY;
+  if (BOUNDED && a.knorm && !indexed && ntiles > 1) {
+    const int rt0 = um.kv_begin / kNormRows, rt1 = (um.kv_begin + n_kv - 1) / kNormRows;
+    const float* kn = a.knorm + static_cast<int64_t>(h) * a.knorm_tiles;
+    float k2 = 0.f;
+    for (int base = rt0; base <= rt1; base += 4 * 64) {
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rt = base + u * 64 + lane;
+        e[u] = rt <= rt1 ? kn[rt] : 0.f;
+      }
+      k2 = fmaxf(k2, fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, off));
+    float q2 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = static_cast<float>(qf[kk][j]);
+        q2 = fmaf(x, x, q2);
+      }
+    qbound = sqrtf(halves_sum(q2) * k2) * sl2 * kBoundSlack;
+  }
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
@@ -186,7 +222,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
       }
   };
   // online softmax of tile t, one query per lane (key halves split across the lane halves)
-  auto softmax_step = [&](int t) {
+  auto softmax_step = [&](int t, auto settled_tag) {
+    constexpr bool SETTLED = decltype(settled_tag)::value;
     if ((t + 1) * BN > n_kv) {
       // The partial last tile: keys past the list get -inf.  Element (kb, r) of this
       // lane is key t*BN + c + 4*half with c = 32 kb + 8 (r/4) + r%4; it is masked
@@ -202,33 +239,35 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
           sacc[kb][r] += __int_as_float(~((c - lim) >> 31) & static_cast<int>(0xff800000u));
         }
     }
-    float mx[KB];
+    if constexpr (!SETTLED) {
+      float mx[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      // At d = 128 a chain of v_max3 (two elements an instruction, 8 per 16): the empty asm
-      // keeps the compiler from rebalancing it into a tree with two-operand maxima (11 per
-      // 16).  At d <= 64, where one item's chain of key tiles sets the time of small batches,
-      // the compiler's shallower tree stays (the same maximum either way).
-      float m = max3f(sacc[kb][0], sacc[kb][1], sacc[kb][2]);
+      for (int kb = 0; kb < KB; ++kb) {
+        // At d = 128 a chain of v_max3 (two elements an instruction, 8 per 16): the empty asm
+        // keeps the compiler from rebalancing it into a tree with two-operand maxima (11 per
+        // 16).  At d <= 64, where one item's chain of key tiles sets the time of small batches,
+        // the compiler's shallower tree stays (the same maximum either way).
+        float m = max3f(sacc[kb][0], sacc[kb][1], sacc[kb][2]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) {
-        if constexpr (D == 128) asm volatile("" : "+v"(m));
-        m = max3f(m, sacc[kb][r], sacc[kb][r + 1]);
+        for (int r = 3; r < 15; r += 2) {
+          if constexpr (D == 128) asm volatile("" : "+v"(m));
+          m = max3f(m, sacc[kb][r], sacc[kb][r + 1]);
+        }
+        mx[kb] = fmaxf(m, sacc[kb][15]);
       }
-      mx[kb] = fmaxf(m, sacc[kb][15]);
-    }
 #pragma unroll
-    for (int w = 1; w < KB; w <<= 1)
+      for (int w = 1; w < KB; w <<= 1)
 #pragma unroll
-      for (int kb = 0; kb + w < KB; kb += 2 * w) mx[kb] = fmaxf(mx[kb], mx[kb + w]);
-    const float tmax = halves_max(mx[0]) * sl2;
-    const bool move = tmax > m_i + kLazyRescale;   // per row: move the reference up
-    if (__any(move)) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_i - tmax) : 1.f;
-      l_i *= alpha;
+        for (int kb = 0; kb + w < KB; kb += 2 * w) mx[kb] = fmaxf(mx[kb], mx[kb + w]);
+      const float tmax = halves_max(mx[0]) * sl2;
+      const bool move = tmax > m_i + kLazyRescale;   // per row: move the reference up
+      if (__any(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_i - tmax) : 1.f;
+        l_i *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m_i = move ? tmax : m_i;
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_i = move ? tmax : m_i;
+      }
     }
     float ls[KB];
 #pragma unroll
@@ -263,7 +302,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     }
   };
 
-  auto tile = [&](int t, auto cur_tag) {
+  auto tile = [&](int t, auto cur_tag, auto settled_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     if constexpr (PAIRS) {
       if constexpr (CUR % 2 == 0) {
@@ -307,7 +346,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
       for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) vts[ks][db] = vt_at(cur_tag, ks, db);
-      softmax_step(t);
+      softmax_step(t, settled_tag);
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
         const int kb = ks >> 1, s8 = (ks & 1) * 8;
@@ -320,21 +359,41 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
       }
     } else {
       s_step(cur_tag);
-      softmax_step(t);
+      softmax_step(t, settled_tag);
       pv_step(cur_tag);
     }
   };
-  // One loop, NS tiles per trip, so that tile t always uses stage t % NS as a
-  // compile-time constant; the tiles past the end of the list are skipped.
-  for (int t = 0; t < ntiles; t += NS) {
-    tile(t, C0{});
-    if (t + 1 < ntiles) tile(t + 1, C1{});
+  // NS tiles per trip, so that tile t always uses stage t % NS as a compile-time
+  // constant; the tiles past the end of the list are skipped.
+  auto trip = [&](int t, auto settled_tag) {
+    tile(t, C0{}, settled_tag);
+    if (t + 1 < ntiles) tile(t + 1, C1{}, settled_tag);
     if constexpr (NS > 2) {
-      if (t + 2 < ntiles) tile(t + 2, C2{});
+      if (t + 2 < ntiles) tile(t + 2, C2{}, settled_tag);
     }
     if constexpr (NS > 3) {
-      if (t + 3 < ntiles) tile(t + 3, C3{});
+      if (t + 3 < ntiles) tile(t + 3, C3{}, settled_tag);
     }
+  };
+  // Trips form each tile's maximum until every row of the wave is settled (its reference
+  // within kLazyRescale of its bound; tested after each trip, on finite bounds only, as an
+  // integer test since this file is compiled without NaN semantics); the remaining trips
+  // skip the maximum.  Two loops rather than a branch inside one: a branch around the
+  // maximum keeps the compiler from scheduling across it (d = 128 then spills).  Every
+  // trip has the same barriers in either loop, so the waves of a workgroup may change
+  // loops at different trips.
+  int t = 0;
+  for (; t < ntiles; t += NS) {
+    trip(t, std::false_type{});
+    if constexpr (BOUNDED) {
+      if (__all((__float_as_uint(qbound) < 0x7f800000u) & (qbound <= m_i + kLazyRescale))) {
+        t += NS;
+        break;
+      }
+    }
+  }
+  if constexpr (BOUNDED) {
+    for (; t < ntiles; t += NS) trip(t, std::true_type{});
   }
   // both lane halves hold partial sums of the same query
   float l_tot = halves_sum(l_i);

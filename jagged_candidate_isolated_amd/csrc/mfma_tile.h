@@ -190,6 +190,13 @@ struct Stages {
 // on the other rows of its wave.
 constexpr float kLazyRescale = 8.f;
 
+// Slack on the Cauchy-Schwarz bound of a row's scores (q.k <= |q| |k|) against the
+// rounding of the computed quantities: the fp32 score of a d <= 128 product of bf16
+// features exceeds the exact one by at most a relative d * 2^-24 of |q| |k|, and the
+// squared norms, square root and products of the bound lose a few times that; 2^-7
+// covers both with room to spare.
+constexpr float kBoundSlack = 1.0078125f;
+
 // Direct-to-LDS loads of K/V tiles (BN keys of D bf16) by NT threads.  Load i of
 // wave w fills LDS slots (w*LOADS + i)*64 + lane; slot -> (row, chunk position) ->
 // global chunk.  A full tile of a contiguous key list is one byte range: a buffer

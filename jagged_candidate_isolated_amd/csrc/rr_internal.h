@@ -25,6 +25,7 @@ constexpr int kZeroHead = 1023;  // ... and head 1023 marks "zero these padding 
 constexpr int kMaxHeads = 1023;
 constexpr int64_t kMaxTiles = int64_t(1) << 21;   // ... and the query tile into the 21 bits above
 constexpr int kSortMax = 2048;   // users planned (and sorted) in LDS by the work-list builder
+constexpr int kNormRows = 64;    // key rows per entry of the key-norm bounds (k_key_norms)
 
 // What one user contributes to an attention call.  Query and key lists are
 // either plain row ranges or, when `idx` is used, ranges of an index array that
@@ -67,8 +68,10 @@ struct WsLayout {
   size_t start;      // int32[B + 1] item starts per sorted user
   size_t idx;        // int32[T] compacted row lists
   size_t items;      // int2[item_bound]
+  size_t knorm;      // float[H][knorm_tiles]: per 64 key rows, the largest squared key norm
   size_t total;
   int64_t item_bound;
+  int64_t knorm_tiles;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -113,6 +116,8 @@ inline WsLayout ws_layout(int64_t B, int64_t T_idx, int64_t q_rows, int64_t H) {
   w.idx = off; off = align256(off + sizeof(int32_t) * size_t(T_idx));
   w.item_bound = item_upper_bound(B, q_rows, H);
   w.items = off; off = align256(off + sizeof(int2) * size_t(w.item_bound));
+  w.knorm_tiles = (T_idx + kNormRows - 1) / kNormRows;
+  w.knorm = off; off = align256(off + sizeof(float) * size_t(H) * size_t(w.knorm_tiles));
   w.total = off;
   return w;
 }
@@ -141,6 +146,9 @@ struct AttnArgs {
   double rope_log2_base;      // != 0: rotate each query row in registers first (log2 of the base);
                               // full sequence without padding: position min(row - start, n_kv),
                               // candidate-only: position n_kv (the frozen history's length)
+  const float* knorm;         // full-sequence plans without idx[]: k_key_norms' bounds for this k,
+                              // [H][knorm_tiles]; NULL = none (every key tile forms its maximum)
+  int32_t knorm_tiles;
 };
 
 // The work item of workgroup slot `item` and its user: false when the plan in the
@@ -420,6 +428,10 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
                            int B, int H, int bm, int rows, int kv_rows, int cap, UserMeta* meta,
                            int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
+// a.knorm[h][t] = the largest squared norm, in head h, of the key rows among rows
+// [64 t, 64 t + 64) of a.k, for a full-sequence plan without idx[] (rows that are no user's key
+// count 0); `rows` = the K rows, d = head width
+hipError_t launch_key_norms(const AttnArgs& a, int rows, int d, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma_self_planned(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
 // the backward: k_bwd_dq over plan aq (tiles of bm_q query rows), k_bwd_dkdv over plan ak

@@ -254,3 +254,44 @@ def test_sentinel_candidate_only(wide):
     ref = A.cand_only_attention(cb.q_cand, cb.k_hist, cb.v_hist, cb.k_cand, cb.v_cand, cb.hist_offsets,
                                 cb.cand_offsets)
     assert_close(got, ref, "bf16", f"sentinel candidate-only wide={wide}")
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_key_bound_settling(d):
+    """Planned wide-tile launches bound every row's scores by |q| max|k| (a pass over the
+    keys) and stop forming tile maxima once no tile can move a row's reference.  The long
+    user's heads are built so that waves settle at different points: head 0 holds the
+    standard draw (every wave settles after its first trip), in head 1 the first 200
+    queries are near one direction q0 and key row 1300 is a large multiple of q0 (their
+    reference moves at that key's tile, about 19 log2 units up, and they settle after it,
+    while the other waves of the same query tiles never do), and head 2 has features of
+    scale 2 (bounds far above every reference: no wave settles).  The planned wide-tile
+    output (with the bound) must equal, bit for bit, the self-planned wide tile and both
+    narrow-tile runs (without it), and match the oracle on sampled rows."""
+    alone, batch, L = _long_and_short(d, 3, 1200 + d, (4, 2500, 700))
+    rng = np.random.default_rng(1250 + d)
+    q, k, v = alone.q.copy(), alone.k.copy(), alone.v.copy()
+    q0 = rng.standard_normal(d) / np.sqrt(d)
+    q[:200, 1] = q0 + 0.02 * rng.standard_normal((200, d)) / np.sqrt(d)
+    alpha = 19.0 / (np.log2(np.e) / np.sqrt(d)) / float(q0 @ q0)
+    k[1300, 1] = alpha * q0
+    q[:, 2] *= 2.0 * np.sqrt(d)
+    k[:, 2] *= 2.0 * np.sqrt(d)
+    q, k = _bf16(q), _bf16(k)
+    alone = W.FullBatch(**{**alone.__dict__, "q": q, "k": k, "v": v})
+    batch = W.FullBatch(**{**batch.__dict__, "q": np.concatenate([q, batch.q[L:]]),
+                           "k": np.concatenate([k, batch.k[L:]]), "v": np.concatenate([v, batch.v[L:]])})
+    _log(f"[tiles key bound] d={d} alone T={alone.T} batch B={batch.B} T={batch.T} alpha={alpha:.1f}")
+    da, db = full_dev(alone), full_dev(batch)
+    outs = [_planned(alone, da), run_full(alone, da), run_full(batch, db)[:L], _planned(batch, db)[:L]]
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o, outs[0]), f"variant {i} differs from the bounded wide-tile output"
+    rows = np.r_[0:6, 195:205, 1298:1302, 2500:2504, alone.T - 6:alone.T]
+    for h in range(3):
+        hs = np.full(len(rows), h)
+        ref = A.full_attention_rows(alone.q, alone.k, alone.v, alone.offsets, alone.cand_start, rows, hs)
+        assert_close(outs[0][rows, hs], ref, "bf16", f"key bound, head {h}, sampled")
