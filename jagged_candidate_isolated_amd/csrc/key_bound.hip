@@ -21,7 +21,8 @@ namespace rr {
 namespace {
 
 constexpr int kNormThreads = 256;
-constexpr int kNormUnroll = 4;   // 16-byte loads in flight per thread
+constexpr int kNormUnroll = 8;   // 16-byte loads in flight per thread
+constexpr int kNormGrid = 2048;  // workgroups of a launch (about one round on the chip)
 
 struct KeyNormArgs {
   AttnArgs a;   // the plan (header, meta), k, B, H, rows
@@ -35,76 +36,82 @@ __global__ __launch_bounds__(kNormThreads) void k_key_norms(KeyNormArgs ka) {
   __shared__ unsigned s_max[kMaxHeads];
   __shared__ unsigned long long s_keys;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int r0 = blockIdx.x * kNormRows;
   const PlanHeader p = *a.plan;
   // only a full-sequence plan for this launch, with plain key ranges, has the bounds used
   if (!((p.magic == kPlanMagic) & (p.B == a.B) & (p.H == a.H) & (p.mode == 0) & (p.indexed == 0) &
         (p.rows == a.rows)))
     return;
-  for (int h = tid; h < a.H; h += kNormThreads) s_max[h] = 0u;
-  if (tid < 64) {
-    const int r = r0 + lane;
-    bool key = false;
-    if (r < a.rows) {
-      int lo = 0, hi = a.B - 1;   // the last user whose key range starts at or before r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.meta[mid].kv_begin <= r) lo = mid;
-        else hi = mid - 1;
-      }
-      const UserMeta m = a.meta[lo];
-      key = r >= m.kv_begin && r - m.kv_begin < m.n_kv;
-    }
-    const unsigned long long keys = __ballot(key);
-    if (lane == 0) s_keys = keys;
-  }
-  __syncthreads();
-  const unsigned long long keys = s_keys;
-  if (keys != 0) {
-    // chunk c of the tile: row c / (H * CH), head (c / CH) % H, 8 features from (c % CH) * 8;
-    // consecutive threads read consecutive 16 bytes
-    const int per_row = a.H * CH;
-    const int n = kNormRows * per_row;
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + int64_t(r0) * a.H * D);
-    for (int c0 = 0; c0 < n; c0 += kNormThreads * kNormUnroll) {
-      uint4 w[kNormUnroll];
-      bool live[kNormUnroll];
-#pragma unroll
-      for (int u = 0; u < kNormUnroll; ++u) {
-        const int c = c0 + u * kNormThreads + tid;
-        const int row = min(c / per_row, kNormRows - 1);
-        live[u] = c < n && ((keys >> row) & 1ull);
-        w[u] = live[u] ? src[c] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kNormUnroll; ++u) {
-        const unsigned x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = __uint_as_float(x[j] << 16), hi = __uint_as_float(x[j] & 0xffff0000u);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
+  const int n_tiles = (a.rows + kNormRows - 1) / kNormRows;
+  const int per_row = a.H * CH;
+  const int n = kNormRows * per_row;   // chunks per tile
+  // grid-stride over the tiles of 64 rows: a launch of about one round of workgroups
+  for (int rt = blockIdx.x; rt < n_tiles; rt += gridDim.x) {
+    const int r0 = rt * kNormRows;
+    for (int h = tid; h < a.H; h += kNormThreads) s_max[h] = 0u;
+    if (tid < 64) {
+      const int r = r0 + lane;
+      bool key = false;
+      if (r < a.rows) {
+        int lo = 0, hi = a.B - 1;   // the last user whose key range starts at or before r
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (a.meta[mid].kv_begin <= r) lo = mid;
+          else hi = mid - 1;
         }
-        // the CH threads of one (row, head) are consecutive lanes starting at a multiple of CH
+        const UserMeta m = a.meta[lo];
+        key = r >= m.kv_begin && r - m.kv_begin < m.n_kv;
+      }
+      const unsigned long long keys = __ballot(key);
+      if (lane == 0) s_keys = keys;
+    }
+    __syncthreads();
+    const unsigned long long keys = s_keys;
+    if (keys != 0) {
+      // chunk c of the tile: row c / (H * CH), head (c / CH) % H, 8 features from (c % CH) * 8;
+      // consecutive threads read consecutive 16 bytes
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + int64_t(r0) * a.H * D);
+      for (int c0 = 0; c0 < n; c0 += kNormThreads * kNormUnroll) {
+        uint4 w[kNormUnroll];
+        bool live[kNormUnroll];
 #pragma unroll
-        for (int off = CH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        const int c = c0 + u * kNormThreads + tid;
-        if (live[u] && (c % CH) == 0) atomicMax(&s_max[(c / CH) % a.H], __float_as_uint(ss));
+        for (int u = 0; u < kNormUnroll; ++u) {
+          const int c = c0 + u * kNormThreads + tid;
+          const int row = min(c / per_row, kNormRows - 1);
+          live[u] = c < n && ((keys >> row) & 1ull);
+          w[u] = live[u] ? src[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kNormUnroll; ++u) {
+          const unsigned x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+          float ss = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float lo = __uint_as_float(x[j] << 16), hi = __uint_as_float(x[j] & 0xffff0000u);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+          }
+          // the CH threads of one (row, head) are consecutive lanes starting at a multiple of CH
+#pragma unroll
+          for (int off = CH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+          const int c = c0 + u * kNormThreads + tid;
+          if (live[u] && (c % CH) == 0) atomicMax(&s_max[(c / CH) % a.H], __float_as_uint(ss));
+        }
       }
     }
+    __syncthreads();
+    // squared norms are >= 0, so their bit patterns order as the values do (NaN above +inf)
+    for (int h = tid; h < a.H; h += kNormThreads)
+      ka.out[int64_t(h) * a.knorm_tiles + rt] = __uint_as_float(s_max[h]);
+    __syncthreads();   // s_max and s_keys are reused by the next tile
   }
-  __syncthreads();
-  // squared norms are >= 0, so their bit patterns order as the values do (NaN above +inf)
-  for (int h = tid; h < a.H; h += kNormThreads)
-    ka.out[int64_t(h) * a.knorm_tiles + blockIdx.x] = __uint_as_float(s_max[h]);
 }
 
 }  // namespace
 
 hipError_t launch_key_norms(const AttnArgs& a, int rows, int d, hipStream_t s) {
-  const int64_t grid = (int64_t(rows) + kNormRows - 1) / kNormRows;
-  if (a.B <= 0 || a.H <= 0 || !a.knorm || grid > a.knorm_tiles) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t(rows) + kNormRows - 1) / kNormRows;
+  if (a.B <= 0 || a.H <= 0 || !a.knorm || tiles > a.knorm_tiles || rows != a.rows) return hipErrorInvalidValue;
+  const int64_t grid = tiles < kNormGrid ? tiles : kNormGrid;
   // the bounds area is the caller's workspace, written here and read by the attention launch
   const KeyNormArgs ka{a, const_cast<float*>(a.knorm)};
   switch (d) {
