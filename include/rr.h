@@ -152,7 +152,8 @@ int rr_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, const
  * rr_attn_fwd_noalloc -- rr_attn_fwd for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
  * takes no workspace and allocates nothing (no hipMalloc, hipFree or allocating library
- * call): the plan lives in a static device array of rr_attn_fwd_noalloc_max_bytes()
+ * call): what rr_attn_fwd keeps in its workspace (the plan, and the key-norm bounds of
+ * wide-tile batches) lives in a static device array of rr_attn_fwd_noalloc_max_bytes()
  * bytes (16 MiB), one copy per GPU, held until the process ends.
  *   arguments, layouts, ownership, stream semantics: as rr_attn_fwd (the caller passes
  *     inputs and outputs; the current device must be the stream's device)
@@ -160,7 +161,8 @@ int rr_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, const
  *     exceeds rr_attn_fwd_noalloc_max_bytes(); RR_EHIP if the array's device address
  *     cannot be looked up
  *   concurrency: every call on a GPU shares that GPU's array; calls in stream order are
- *     independent (each rewrites the whole plan), calls that overlap on one GPU race.
+ *     independent (each rewrites the whole plan and the bounds it reads), calls that overlap
+ *     on one GPU race.
  */
 size_t rr_attn_fwd_noalloc_max_bytes(void);
 int rr_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, const int32_t* offsets,

@@ -1,15 +1,17 @@
 // Full-sequence forward for callers that cannot allocate device memory (code under
 // HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
-// plan and kernels as rr_attn_fwd, with the plan kept in a file-scope device array
-// instead of a caller-provided workspace.
+// plan and kernels as rr_attn_fwd, with what rr_attn_fwd keeps in its workspace (the plan,
+// and for wide-tile batches the key-norm bounds) in a file-scope device array instead of a
+// caller-provided workspace.
 //
 // Each GPU the library runs on holds its own copy of the array (kScratchBytes) until the
 // process ends.  Host code never uses the array's name as an address: on the first
 // call on a device (with that device current) the device address is looked up with
 // hipGetSymbolAddress and kept per device.  Every call on a GPU shares that GPU's array
-// and overwrites the plan the previous call left there; the plan is rewritten in full
-// by every call (nothing in it must start at zero), so calls in stream order are
-// independent, while calls that overlap on one GPU (other streams or threads) race.
+// and overwrites the plan the previous call left there; the plan, and any bounds a call
+// reads, are rewritten in full by that call (nothing must start at zero), so calls in
+// stream order are independent, while calls that overlap on one GPU (other streams or
+// threads) race.
 #include <mutex>
 
 #include "rr_internal.h"
