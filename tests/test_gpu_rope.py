@@ -138,18 +138,21 @@ def test_rope_cand_only_equals_full_rows():
 # ---------------------------------------------------------------- queries rotated inside the attention
 
 
-@pytest.mark.parametrize("d,wide", [(32, False), (64, False), (128, False), (64, True), (128, True)])
-def test_fused_query_rotation_equals_the_rotary_pass(d, wide):
+@pytest.mark.parametrize("d,wide,H", [(32, False, 3), (64, False, 3), (128, False, 3), (64, True, 2), (128, True, 2),
+                                      (128, True, 32)])
+def test_fused_query_rotation_equals_the_rotary_pass(d, wide, H):
     """rr_attn_fwd_rope (q rotated in the kernel's registers) gives the same bits as
     rr_rope_qk followed by rr_attn_fwd, on the in-kernel-plan path and the separate plan,
-    narrow and wide tiles; and it matches the rotary oracle."""
-    rng = np.random.default_rng(600 + d + wide)
+    narrow and wide tiles; and it matches the rotary oracle.  With 32 heads the wide batch
+    is planned separately in every call, so the rotating kernel also runs with the key-norm
+    bound (its bound taken from the rotated queries)."""
+    rng = np.random.default_rng(600 + d + wide + H)
     if wide:
-        fb = W.make_full_batch(rng, "rope-fused-wide", prefix=[3, 1], hist=[3000, 2200], cand=[1500, 2100], H=2, d=d,
-                               seed=610 + d)
+        fb = W.make_full_batch(rng, "rope-fused-wide", prefix=[3, 1], hist=[3000, 2200], cand=[1500, 2100], H=H, d=d,
+                               seed=610 + d + H)
     else:
         fb = W.make_full_batch(rng, "rope-fused", prefix=[4, 0, 2, 1], hist=[700, 0, 57, 260], cand=[33, 9, 0, 129],
-                               H=3, d=d, seed=620 + d)
+                               H=H, d=d, seed=620 + d)
     assert (fb.T >= 2048 * fb.B) == wide
     dv = full_dev(fb)
     base = 500.0
