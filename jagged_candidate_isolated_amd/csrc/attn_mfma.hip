@@ -146,6 +146,48 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
     }
   }
 
+  // the barrier before tile t and the loads it frees a stage for
+  auto pipeline_step = [&](int t, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    if constexpr (PAIRS) {
+      if constexpr (CUR % 2 == 0) {
+        // tiles t and t+1 have landed once none of this wave's loads is outstanding; past
+        // the barrier every wave's loads are visible and every wave is done with tiles
+        // t-2 and t-1, whose stages take t+2 and t+3
+        wait_vmem<0>();
+        tile_barrier();
+        if (t + 2 < ntiles) issue_tile(t + 2, std::integral_constant<int, (CUR + 2) % NS>{});
+        if (t + 3 < ntiles) issue_tile(t + 3, std::integral_constant<int, (CUR + 3) % NS>{});
+      }
+    } else {
+      // Tile t has landed once no more than the loads of the tiles issued after it are
+      // outstanding (this wave's loads, retiring in order); the barrier makes every
+      // wave's loads visible and tells that every wave is done with the stage of tile
+      // t+AHEAD, refilled next to overlap the following tiles' math.
+      wait_tiles<LPT>(min(AHEAD - 1, ntiles - 1 - t));
+      tile_barrier();
+      if (t + AHEAD < ntiles) issue_tile(t + AHEAD, std::integral_constant<int, (CUR + AHEAD) % NS>{});
+    }
+  };
+  // A wave whose rows all lie past the user's query list (in the last query tile of a user)
+  // computes nothing: it issues its share of every tile's loads, which the other waves
+  // read, and meets every barrier, then stops (no load of its own is outstanding then).
+  // (Not in the planned narrow kernels at d <= 64: there the extra path takes them past
+  // 128 VGPRs, a wave per SIMD.)
+  constexpr bool SKIP_DEAD = NW * kQw == kBmMfmaWide || EAGER;
+  if (SKIP_DEAD && __all(!qvalid)) {
+    for (int u = 0; u < ntiles; u += NS) {
+      pipeline_step(u, C0{});
+      if (u + 1 < ntiles) pipeline_step(u + 1, C1{});
+      if constexpr (NS > 2) {
+        if (u + 2 < ntiles) pipeline_step(u + 2, C2{});
+      }
+      if constexpr (NS > 3) {
+        if (u + 3 < ntiles) pipeline_step(u + 3, C3{});
+      }
+    }
+    return;
+  }
   // A bound on this row's scaled scores against every key of the user, |q| max|k| (the
   // key-norm pass gives max|k|^2 per 64 key rows and head), or +inf without one.  Once
   // every row of the wave has its reference within kLazyRescale of its bound, no later
@@ -304,25 +346,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
 
   auto tile = [&](int t, auto cur_tag, auto settled_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
-    if constexpr (PAIRS) {
-      if constexpr (CUR % 2 == 0) {
-        // tiles t and t+1 have landed once none of this wave's loads is outstanding; past
-        // the barrier every wave's loads are visible and every wave is done with tiles
-        // t-2 and t-1, whose stages take t+2 and t+3
-        wait_vmem<0>();
-        tile_barrier();
-        if (t + 2 < ntiles) issue_tile(t + 2, std::integral_constant<int, (CUR + 2) % NS>{});
-        if (t + 3 < ntiles) issue_tile(t + 3, std::integral_constant<int, (CUR + 3) % NS>{});
-      }
-    } else {
-      // Tile t has landed once no more than the loads of the tiles issued after it are
-      // outstanding (this wave's loads, retiring in order); the barrier makes every
-      // wave's loads visible and tells that every wave is done with the stage of tile
-      // t+AHEAD, refilled next to overlap the following tiles' math.
-      wait_tiles<LPT>(min(AHEAD - 1, ntiles - 1 - t));
-      tile_barrier();
-      if (t + AHEAD < ntiles) issue_tile(t + AHEAD, std::integral_constant<int, (CUR + AHEAD) % NS>{});
-    }
+    pipeline_step(t, cur_tag);
     if constexpr (EAGER) {
       // the same products with every LDS operand read issued early: all K operands before
       // the S products, all V^T operands right after them, so that their latency passes
