@@ -272,6 +272,27 @@ def test_many_users_cached_request_bit_identical():
     assert np.all(np.isfinite(_np(xc))) and np.all(np.isfinite(_np(xh)))
 
 
+def test_long_users_cached_request_bit_identical():
+    """Users of about 4000 rows: the full layers run on 256-row query tiles with the
+    key-norm bound (their tiles stop forming maxima once no key can move a row's
+    reference), while the cached request's candidate-only layers run on 128-row tiles
+    without it.  The cached request still reproduces the full request's candidates bit
+    for bit."""
+    shapes = dict(prefix=[4, 2], hist=[3000, 2600], cand=[900, 1500])
+    H, d, n_layers, nco = 4, 128, 4, 2
+    x, off, cs, dl, _ = _setup(H, d, n_layers, seed=64, shapes=shapes)
+    T, B = int(off[-1]), len(shapes["hist"])
+    assert T >= 2048 * B, "the full layers must take the wide tile"
+    print(f"[ranker, long users] B={B} T={T}", flush=True)
+    _, xc, xh, cache = _run(x, off, cs, dl, nco, H, d)
+    xh0, xc0, hoff, coff = RK.split_history_and_candidates(x, off, cs)
+    again = rr().rr_ranker_cached_fwd(to_dev(xc0.astype(np.float32)), dl, cache, to_dev(hoff.astype(np.int32)),
+                                      to_dev(coff.astype(np.int32)), H, d)
+    torch.cuda.synchronize()
+    assert torch.equal(again, xc)
+    assert np.all(np.isfinite(_np(xc))) and np.all(np.isfinite(_np(xh)))
+
+
 def test_candidate_order_bit_identical():
     H, d, n_layers, nco = 4, 64, 3, 1
     x, off, cs, dl, _ = _setup(H, d, n_layers, seed=70)
