@@ -201,8 +201,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const int2 it, cons
   // kernels the second loop below costs registers -- at d = 64 a wave per SIMD.)
   constexpr bool BOUNDED = NW * kQw == kBmMfmaWide;
   float qbound = INFINITY;
-  if (BOUNDED && a.knorm && !indexed && ntiles > 1) {
-    const int rt0 = um.kv_begin / kNormRows, rt1 = (um.kv_begin + n_kv - 1) / kNormRows;
+  if (BOUNDED && a.knorm && ntiles > 1) {
+    // the span of the user's key rows: its key range, or the first and last rows of its list
+    const bool direct = !indexed || um.kv_direct;
+    const int first = direct ? um.kv_begin : a.idx[um.kv_begin];
+    const int last = direct ? um.kv_begin + n_kv - 1 : a.idx[um.kv_begin + n_kv - 1];
+    const int rt0 = first / kNormRows, rt1 = last / kNormRows;
     const float* kn = a.knorm + static_cast<int64_t>(h) * a.knorm_tiles;
     float k2 = 0.f;
     for (int base = rt0; base <= rt1; base += 4 * 64) {

@@ -10,11 +10,13 @@
 // product and the exponentials.
 //
 // This pass supplies the key side of that bound: for every 64 rows of k and every head,
-// the largest squared norm among the rows that are some user's keys.  A user's key rows
-// are one range of the full-sequence plan (prefix and history rows), so a row is a key
-// exactly when it lies in the key range of the last user whose range starts at or before
-// it.  Candidate-only rows are skipped (no query reads them through the key loop), so
-// the pass reads about the key rows' bytes once.
+// the largest squared norm among the rows in some user's key span.  A user's rows start at
+// its query-list start in either kind of full-sequence plan, so the last user whose list
+// starts at or before a row owns it; the row counts when it lies between that user's first
+// and last key rows (its key range, or for a padded batch the first and last rows of its
+// listed keys: any padding between them only loosens the bound).  Candidate rows are
+// skipped (no query reads them through the key loop), so the pass reads about the key
+// rows' bytes once.
 #include "rr_internal.h"
 
 namespace rr {
@@ -37,10 +39,9 @@ __global__ __launch_bounds__(kNormThreads) void k_key_norms(KeyNormArgs ka) {
   __shared__ unsigned long long s_keys;
   const int tid = threadIdx.x, lane = tid & 63;
   const PlanHeader p = *a.plan;
-  // only a full-sequence plan for this launch, with plain key ranges, has the bounds used
-  if (!((p.magic == kPlanMagic) & (p.B == a.B) & (p.H == a.H) & (p.mode == 0) & (p.indexed == 0) &
-        (p.rows == a.rows)))
-    return;
+  // only a full-sequence plan for this launch has the bounds used
+  if (!((p.magic == kPlanMagic) & (p.B == a.B) & (p.H == a.H) & (p.mode == 0) & (p.rows == a.rows))) return;
+  const bool listed = p.indexed != 0;
   const int n_tiles = (a.rows + kNormRows - 1) / kNormRows;
   const int per_row = a.H * CH;
   const int n = kNormRows * per_row;   // chunks per tile
@@ -52,14 +53,19 @@ __global__ __launch_bounds__(kNormThreads) void k_key_norms(KeyNormArgs ka) {
       const int r = r0 + lane;
       bool key = false;
       if (r < a.rows) {
-        int lo = 0, hi = a.B - 1;   // the last user whose key range starts at or before r
+        int lo = 0, hi = a.B - 1;   // the last user whose rows start at or before r
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
-          if (a.meta[mid].kv_begin <= r) lo = mid;
+          if (a.meta[mid].q_begin <= r) lo = mid;
           else hi = mid - 1;
         }
         const UserMeta m = a.meta[lo];
-        key = r >= m.kv_begin && r - m.kv_begin < m.n_kv;
+        if (m.n_kv > 0) {
+          const bool direct = !listed || m.kv_direct;
+          const int first = direct ? m.kv_begin : a.idx[m.kv_begin];
+          const int last = direct ? m.kv_begin + m.n_kv - 1 : a.idx[m.kv_begin + m.n_kv - 1];
+          key = r >= first && r <= last;
+        }
       }
       const unsigned long long keys = __ballot(key);
       if (lane == 0) s_keys = keys;

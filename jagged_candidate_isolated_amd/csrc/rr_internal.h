@@ -146,7 +146,7 @@ struct AttnArgs {
   double rope_log2_base;      // != 0: rotate each query row in registers first (log2 of the base);
                               // full sequence without padding: position min(row - start, n_kv),
                               // candidate-only: position n_kv (the frozen history's length)
-  const float* knorm;         // full-sequence plans without idx[]: k_key_norms' bounds for this k,
+  const float* knorm;         // full-sequence plans: k_key_norms' bounds for this k,
                               // [H][knorm_tiles]; NULL = none (every key tile forms its maximum)
   int32_t knorm_tiles;
 };
@@ -428,9 +428,9 @@ hipError_t launch_worklist(int mode, const int32_t* offs_a, const int32_t* offs_
                            int B, int H, int bm, int rows, int kv_rows, int cap, UserMeta* meta,
                            int32_t* start, int2* items, PlanHeader* header, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int d, int dtype, int64_t grid, hipStream_t s);
-// a.knorm[h][t] = the largest squared norm, in head h, of the key rows among rows
-// [64 t, 64 t + 64) of a.k, for a full-sequence plan without idx[] (rows that are no user's key
-// count 0); `rows` = the K rows, d = head width
+// a.knorm[h][t] = the largest squared norm, in head h, of the rows among rows [64 t, 64 t + 64)
+// of a.k that lie in some user's key span (from its first to its last key row), for a
+// full-sequence plan (other rows count 0); `rows` = the K rows, d = head width
 hipError_t launch_key_norms(const AttnArgs& a, int rows, int d, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);
 hipError_t launch_attn_mfma_self_planned(const AttnArgs& a, int d, int bm, int64_t grid, hipStream_t s);

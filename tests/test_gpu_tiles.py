@@ -295,3 +295,51 @@ def test_key_bound_settling(d):
         hs = np.full(len(rows), h)
         ref = A.full_attention_rows(alone.q, alone.k, alone.v, alone.offsets, alone.cand_start, rows, hs)
         assert_close(outs[0][rows, hs], ref, "bf16", f"key bound, head {h}, sampled")
+
+
+@pytest.mark.parametrize("flag", [False, True])
+def test_key_bound_settling_padded(flag):
+    """The key-norm bound on padded batches: a long user with 50 padding rows between its
+    prefix and its history, the heads built as in test_key_bound_settling (waves settling
+    early, late and never).  Attended padding (flag True) keeps the keys one row range;
+    excluded padding (flag False) lists them through the compacted rows, and the bound then
+    spans the first to the last listed key.  The planned wide-tile output must equal, bit
+    for bit, the same user's rows in a batch of short users on the narrow tile, and match
+    the oracle on sampled rows (padding rows excluded from the keys read 0)."""
+    d, H, P = 128, 3, 50
+    rng = np.random.default_rng(1300 + flag)
+    alone = W.make_full_batch(rng, "pad-long", prefix=[4], hist=[2500], cand=[700], pad=[P], H=H, d=d,
+                              attend_padded_history=flag, seed=1310 + flag)
+    q, k, v = alone.q.copy(), alone.k.copy(), alone.v.copy()
+    q0 = rng.standard_normal(d) / np.sqrt(d)
+    q[:200, 1] = q0 + 0.02 * rng.standard_normal((200, d)) / np.sqrt(d)
+    k[1300, 1] = 19.0 / (np.log2(np.e) / np.sqrt(d)) / float(q0 @ q0) * q0
+    q[:, 2] *= 2.0 * np.sqrt(d)
+    k[:, 2] *= 2.0 * np.sqrt(d)
+    q, k = _bf16(q), _bf16(k)
+    alone = W.FullBatch(**{**alone.__dict__, "q": q, "k": k, "v": v})
+    n_short = 40
+    sp, sh, sc = rng.integers(0, 4, n_short), rng.integers(0, 60, n_short), rng.integers(0, 12, n_short)
+    short = W.make_full_batch(rng, "short", prefix=sp, hist=sh, cand=sc, pad=rng.integers(0, 3, n_short), H=H,
+                              d=d, attend_padded_history=flag, seed=1320 + flag)
+    L = alone.T
+    off = np.concatenate([alone.offsets, short.offsets[1:] + L]).astype(np.int32)
+    cst = np.concatenate([alone.cand_start, short.cand_start + L]).astype(np.int32)
+    valid = np.concatenate([alone.valid, short.valid]).astype(np.uint8)
+    batch = W.FullBatch(**{**short.__dict__, "name": "pad-mixed", "prefix": np.r_[alone.prefix, short.prefix],
+                           "hist": np.r_[alone.hist, short.hist], "cand": np.r_[alone.cand, short.cand],
+                           "pad": np.r_[alone.pad, short.pad], "offsets": off, "cand_start": cst, "valid": valid,
+                           "q": np.concatenate([q, short.q]), "k": np.concatenate([k, short.k]),
+                           "v": np.concatenate([v, short.v])})
+    assert alone.T >= WIDE_ROWS * alone.B and batch.T < WIDE_ROWS * batch.B
+    _log(f"[tiles key bound padded] flag={flag} alone T={alone.T} batch B={batch.B} T={batch.T}")
+    da, db = full_dev(alone), full_dev(batch)
+    outs = [_planned(alone, da), run_full(alone, da), run_full(batch, db)[:L], _planned(batch, db)[:L]]
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o, outs[0]), f"variant {i} differs from the bounded wide-tile output"
+    rows = np.r_[0:6, 50:56, 195:205, 1298:1302, 2550:2556, alone.T - 6:alone.T]
+    for h in range(H):
+        hs = np.full(len(rows), h)
+        ref = A.full_attention_rows(alone.q, alone.k, alone.v, alone.offsets, alone.cand_start, rows, hs,
+                                    valid=alone.valid, attend_padded_history=flag)
+        assert_close(outs[0][rows, hs], ref, "bf16", f"padded key bound, flag {flag}, head {h}, sampled")
