@@ -290,5 +290,68 @@ def pin_layer_rounding_sigma():
     L = RK.Layer(layers[0].gain, layers[0].w_qkv, np.zeros((H * d, H * d)))
     assert np.all(RK.full_layer_rounding_sigma(x, L, off, cs, H, d, base, samples=4) == 0)
 
+def _float32_layer(x, L, offsets, cand_start, H, d, base):
+    """One full-sequence layer computed entirely in float32 torch, written here (angles in
+    float64, then cast): the float32-level arithmetic that ``f32_slack`` bounds.  Returns the
+    new x in float64."""
+    import torch
+    import torch.nn.functional as F
+    T, D = x.shape
+    f = torch.float32
+    X = torch.from_numpy(np.asarray(x, np.float32))
+    h = F.rms_norm(X, (D,), weight=torch.from_numpy(np.asarray(L.gain, np.float32)), eps=RK.RMS_EPS)
+    q, k, v = F.linear(h, torch.from_numpy(np.asarray(L.w_qkv, np.float32))).split(D, dim=1)
+    pos = torch.zeros(T, dtype=torch.float64)
+    for b in range(len(cand_start)):
+        lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        for i in range(lo, hi):
+            pos[i] = min(i, cs) - lo
+    inv = base ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    ang = pos[:, None] * inv[None, :]
+    c, s_ = torch.cos(ang).to(f)[:, None, :], torch.sin(ang).to(f)[:, None, :]
+
+    def rot(t):
+        t = t.reshape(T, H, d // 2, 2)
+        a, b2 = t[..., 0], t[..., 1]
+        return torch.stack([a * c - b2 * s_, a * s_ + b2 * c], -1).reshape(T, H, d)
+    q, k, v = rot(q), rot(k), v.reshape(T, H, d)
+    out = torch.zeros(T, H, d, dtype=f)
+    sc = 1.0 / np.sqrt(d)
+    for b in range(len(cand_start)):
+        lo, cs, hi = int(offsets[b]), int(cand_start[b]), int(offsets[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        m = torch.tensor([[j < cs - lo or i == j for j in range(n)] for i in range(n)], dtype=torch.bool)
+        for hh in range(H):
+            s = (sc * q[lo:hi, hh] @ k[lo:hi, hh].T).masked_fill(~m, float("-inf"))
+            w = torch.exp(s - s.max(dim=1, keepdim=True).values)
+            out[lo:hi, hh] = (w @ v[lo:hi, hh]) / w.sum(dim=1, keepdim=True)
+    return (X + F.linear(out.reshape(T, D), torch.from_numpy(np.asarray(L.w_o, np.float32)))).numpy().astype(np.float64)
+
+
+def pin_f32_slack():
+    """``f32_slack`` against a layer computed entirely in float32 here: element by element
+    the float32 layer stays within the slack of the float64 oracle layer, and the slack is
+    not vacuous (on a sharp softmax the float32 error reaches more than a third of it).
+    Three shapes, a flat and a sharp softmax, and a residual stream scaled by 1000 (the
+    normalised layer's update does not change, the residual add's rounding grows)."""
+    base = 50.0
+    worst = 0.0
+    for seed, H, d, sharp, xs in ((71, 2, 8, 1.0, 1.0), (72, 2, 8, 4.0, 1.0), (73, 4, 16, 1.0, 1.0),
+                                  (74, 2, 8, 1.0, 1e3)):
+        x, layers, off, cs, H, d = make_stack(seed, n_layers=1, H=H, d=d)
+        x = x * xs
+        L = RK.Layer(layers[0].gain, layers[0].w_qkv * sharp, layers[0].w_o)
+        ref = RK.block_full(x, L, off, cs, H, d, base)
+        err = np.abs(_float32_layer(x, L, off, cs, H, d, base) - ref)
+        sl = RK.f32_slack(x, L, off, cs, H, d, base)
+        assert sl.shape == ref.shape and np.all(sl > 0)
+        ratio = float(np.max(err / sl))
+        assert ratio <= 1.0, (seed, sharp, xs, ratio)
+        worst = max(worst, ratio)
+    assert worst >= 0.35, worst
+
+
 RANKER_PINS = [pin_rms_norm, pin_torch_stack, pin_user_tokens, pin_closed_forms, pin_invariants,
-               pin_layer_rounding_sigma]
+               pin_layer_rounding_sigma, pin_f32_slack]

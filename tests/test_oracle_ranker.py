@@ -86,3 +86,26 @@ def test_rounding_sigma_mutations_caught(name, monkeypatch):
         monkeypatch.setattr(RK, attr, fn)
     with pytest.raises(AssertionError):
         _ranker_pins.pin_layer_rounding_sigma()
+
+
+def _slack_mutation(kind):
+    """``f32_slack`` with one of its terms mistaken: the float32 unit roundoff a quarter of
+    its value, or the update-relative, the W_o-accumulation or the residual-add term left
+    out."""
+    def slack(x, layer, offsets, cand_start, H, d, base=RK.DEFAULT_BASE, scale=None):
+        upd, o = RK._perturbed_full_layer(x, layer, offsets, cand_start, H, d, base, scale, lambda p, a: a)
+        D = H * d
+        u = RK.U_F32 / 4 if kind == "u_quarter" else RK.U_F32
+        terms = {"accum": (D + 2) * u * (np.abs(o.reshape(len(upd), D)) @ np.abs(np.asarray(layer.w_o)).T),
+                 "resid": 4 * u * np.abs(np.asarray(x, np.float64)),
+                 "upd": (2.0 ** -18 if kind != "u_quarter" else 2.0 ** -20) * np.abs(upd)}
+        dropped = {"no_upd_term": "upd", "no_accum_term": "accum", "no_resid_term": "resid"}.get(kind)
+        return sum(v for k, v in terms.items() if k != dropped) + 1e-300
+    return slack
+
+
+@pytest.mark.parametrize("name", ["u_quarter", "no_upd_term", "no_accum_term", "no_resid_term"])
+def test_f32_slack_mutations_caught(name, monkeypatch):
+    monkeypatch.setattr(RK, "f32_slack", _slack_mutation(name))
+    with pytest.raises(AssertionError):
+        _ranker_pins.pin_f32_slack()
