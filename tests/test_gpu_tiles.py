@@ -36,11 +36,11 @@ def _np(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def _planned(fb, dev):
+def _planned(fb, dev, scale=None):
     """plan + run (the separate planning launch) of a full-sequence batch."""
     ws = rr().rr_attn_plan(dev["offsets"], dev["cand_start"], fb.T, fb.H, fb.d, dev["q"].dtype,
                            valid=dev["valid"], attend_padded_history=fb.attend_padded_history)
-    out = rr().rr_attn_run(dev["q"], dev["k"], dev["v"], fb.B, ws)
+    out = rr().rr_attn_run(dev["q"], dev["k"], dev["v"], fb.B, ws, scale=scale)
     torch.cuda.synchronize()
     return _np(out)
 
@@ -260,8 +260,8 @@ def _bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
-def test_key_bound_settling(d):
+@pytest.mark.parametrize("d,scale", [(32, None), (64, None), (128, None), (128, 0.3)])
+def test_key_bound_settling(d, scale):
     """Planned wide-tile launches bound every row's scores by |q| max|k| (a pass over the
     keys) and stop forming tile maxima once no tile can move a row's reference.  The long
     user's heads are built so that waves settle at different points: head 0 holds the
@@ -271,7 +271,8 @@ def test_key_bound_settling(d):
     while the other waves of the same query tiles never do), and head 2 has features of
     scale 2 (bounds far above every reference: no wave settles).  The planned wide-tile
     output (with the bound) must equal, bit for bit, the self-planned wide tile and both
-    narrow-tile runs (without it), and match the oracle on sampled rows."""
+    narrow-tile runs (without it), and match the oracle on sampled rows; also with a softmax
+    scale of 0.3 instead of 1/sqrt(d) (the bound scales with it)."""
     alone, batch, L = _long_and_short(d, 3, 1200 + d, (4, 2500, 700))
     rng = np.random.default_rng(1250 + d)
     q, k, v = alone.q.copy(), alone.k.copy(), alone.v.copy()
@@ -287,13 +288,15 @@ def test_key_bound_settling(d):
                            "k": np.concatenate([k, batch.k[L:]]), "v": np.concatenate([v, batch.v[L:]])})
     _log(f"[tiles key bound] d={d} alone T={alone.T} batch B={batch.B} T={batch.T} alpha={alpha:.1f}")
     da, db = full_dev(alone), full_dev(batch)
-    outs = [_planned(alone, da), run_full(alone, da), run_full(batch, db)[:L], _planned(batch, db)[:L]]
+    kw = {} if scale is None else {"scale": scale}
+    outs = [_planned(alone, da, scale), run_full(alone, da, **kw), run_full(batch, db, **kw)[:L],
+            _planned(batch, db, scale)[:L]]
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(o, outs[0]), f"variant {i} differs from the bounded wide-tile output"
     rows = np.r_[0:6, 195:205, 1298:1302, 2500:2504, alone.T - 6:alone.T]
     for h in range(3):
         hs = np.full(len(rows), h)
-        ref = A.full_attention_rows(alone.q, alone.k, alone.v, alone.offsets, alone.cand_start, rows, hs)
+        ref = A.full_attention_rows(alone.q, alone.k, alone.v, alone.offsets, alone.cand_start, rows, hs, **kw)
         assert_close(outs[0][rows, hs], ref, "bf16", f"key bound, head {h}, sampled")
 
 
