@@ -33,6 +33,11 @@
 // planning kernel: each workgroup then builds the work list itself (self_plan_item, or
 // self_plan_item_wave per wave for up to 64 users).
 //
+// Two shortcuts that keep every bit: on the wide tile, once a wave's rows can no longer
+// move their softmax reference (a bound on their scores from the key-norm pass), the
+// remaining key tiles skip forming their maximum; and in the narrow d = 128 and
+// self-planned kernels a wave whose rows all lie past the query list only loads and waits.
+//
 // Numerics: bf16 operands, fp32 accumulation, online softmax in fp32 with exp2
 // (scale * log2 e folded into one FMA), P rounded to bf16 for the PV product,
 // output rounded to bf16 (round to nearest even).
