@@ -3,12 +3,16 @@
 
 A step is one pass of the hot path over one batch with its inputs resident in HBM:
 ``rr_attn_plan`` (segment IDs / bounds / length-sorted work list) then ``rr_attn_run``
-(the fused attention kernel) -- or, for a small unpadded batch such as the default
-workload, ``rr_attn_fwd``, whose attention kernel builds the work list itself (one
-launch); for the candidate-only workload ``rr_cand_only_plan`` + ``rr_cand_only_run``.  The default workload is the
-short-history batch (B=64, prefix 4, history log-uniform in [10, 1000], 32
-candidates per user, H=4, d=64, bf16).  Steps rotate over enough copies of the
-inputs (>= 1 GiB in total) that no step finds its data in the 256 MB Infinity Cache.
+(for batches of long users the key-norm pass, then the fused attention kernel) -- or, for
+a small unpadded batch such as the short-history workload, ``rr_attn_fwd``, whose
+attention kernel builds the work list itself (one launch); for the candidate-only
+workload ``rr_cand_only_plan`` + ``rr_cand_only_run``.  The default line times the skew
+workload (B=32, prefix 4, history lengths drawn from {0, 10, 100, 1000, 8192}, 2048
+candidates per user, H=16, d=128, bf16, no padding) against the bf16 MFMA roofline, and
+carries the short-history workload (B=64, prefix 4, history log-uniform in [10, 1000],
+32 candidates per user, H=4, d=64, bf16) with its HBM roofline as a secondary object.
+Steps rotate over ceil(1 GiB / footprint) copies of the inputs (one for a batch above
+1 GiB), so that no step finds its data in the 256 MB Infinity Cache.
 
 metric: effective (non-pad) attention TFLOP/s = 4 * d * H * sum_b [n_b^2 + c_b (n_b + 1)]
 per step / step time; candidates/s is reported beside it.
