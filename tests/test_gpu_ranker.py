@@ -396,3 +396,58 @@ def test_user_token_cached_request_bit_identical():
                                       to_dev(coff.astype(np.int32)), H, d)
     torch.cuda.synchronize()
     assert torch.equal(again, xc)
+
+
+def test_random_stack_sweep():
+    """Seeded random layouts (up to 12 users; empty histories, users without candidates, single
+    candidates, prefix-only histories), H 1-4 and d 32-128 with H d a multiple of 128, 2-3 layers
+    of which 0 to all are
+    candidate-only.  Per batch: each layer's update against the oracle's layer on the GPU's
+    state before it, in relative Frobenius norm; the cached request equal to the full
+    request's candidates bit for bit; and a permutation of one user's candidates permuting
+    their outputs bit for bit.  (Every batch keeps at least one candidate.)"""
+    for i in range(12):
+        rng = np.random.default_rng(7700 + i)
+        B = int(rng.integers(1, 13))
+        shapes = dict(prefix=rng.integers(0, 4, B), hist=rng.integers(0, 300, B) * (rng.random(B) > 0.15),
+                      cand=rng.integers(1, 40, B) * (rng.random(B) > 0.15))
+        if shapes["cand"].sum() == 0:
+            shapes["cand"][0] = 1
+        H, d = [(1, 128), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128)][int(rng.integers(0, 6))]   # D % 128 == 0
+        n_layers = int(rng.integers(2, 4))
+        nco = int(rng.integers(0, n_layers + 1))
+        what = f"stack sweep {i} (B={B} H={H} d={d} layers={n_layers} candidate-only={nco})"
+        print(what, flush=True)
+        x, off, cs, dl, ol = _setup(H, d, n_layers, seed=7800 + i, shapes=shapes)
+        hoff = np.concatenate([[0], np.cumsum(cs - off[:-1])])
+        coff = np.concatenate([[0], np.cumsum(off[1:] - cs)])
+        prev_full, prev_c, prev_h = x.astype(np.float64), None, None
+        n_full = n_layers - nco
+        for l in range(1, n_layers + 1):
+            xd, xc, xh, cache = _run(x, off, cs, dl[:l], max(0, l - n_full), H, d)
+            if l <= n_full:
+                got = _np(xd)
+                _frob(got, RK.block_full(prev_full, ol[l - 1], off, cs, H, d), prev_full, f"{what}, full layer {l}")
+                prev_full = got
+                prev_h, prev_c = RK.split_history_and_candidates(got, off, cs)[:2]
+            else:
+                if prev_c is None:
+                    prev_h, prev_c = RK.split_history_and_candidates(prev_full, off, cs)[:2]
+                assert np.array_equal(_np(xh), prev_h), f"{what}: the history moved"
+                kh, vh = RK.history_kv(prev_h, ol[l - 1], hoff, H, d)
+                got = _np(xc)
+                _frob(got, RK.block_cand_only(prev_c, kh, vh, ol[l - 1], hoff, coff, H, d), prev_c,
+                      f"{what}, candidate-only layer {l}")
+                prev_c = got
+        xc0 = RK.split_history_and_candidates(x, off, cs)[1]
+        again = rr().rr_ranker_cached_fwd(to_dev(xc0.astype(np.float32)), dl, cache, to_dev(hoff.astype(np.int32)),
+                                          to_dev(coff.astype(np.int32)), H, d)
+        torch.cuda.synchronize()
+        assert torch.equal(again, xc), f"{what}: cached request"
+        b = int(np.argmax(off[1:] - cs))
+        perm = np.arange(len(x))
+        perm[cs[b]:off[b + 1]] = cs[b] + rng.permutation(off[b + 1] - cs[b])
+        _, xc2, xh2, _ = _run(x[perm], off, cs, dl, nco, H, d)
+        cperm = np.arange(int(coff[-1]))
+        cperm[coff[b]:coff[b + 1]] = coff[b] + (perm[cs[b]:off[b + 1]] - cs[b])
+        assert torch.equal(xh2, xh) and torch.equal(xc2, xc[to_dev(cperm)]), f"{what}: candidate order"
