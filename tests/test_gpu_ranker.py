@@ -398,24 +398,30 @@ def test_user_token_cached_request_bit_identical():
     assert torch.equal(again, xc)
 
 
+def _random_stack_case(i):
+    """Layout and stack shape of random case i: up to 12 users (empty histories, users without
+    candidates, single candidates, prefix-only histories; at least one candidate), H and d
+    with H d a multiple of 128, 2-3 layers of which 0 to all are candidate-only."""
+    rng = np.random.default_rng(7700 + i)
+    B = int(rng.integers(1, 13))
+    shapes = dict(prefix=rng.integers(0, 4, B), hist=rng.integers(0, 300, B) * (rng.random(B) > 0.15),
+                  cand=rng.integers(1, 40, B) * (rng.random(B) > 0.15))
+    if shapes["cand"].sum() == 0:
+        shapes["cand"][0] = 1
+    H, d = [(1, 128), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128)][int(rng.integers(0, 6))]
+    n_layers = int(rng.integers(2, 4))
+    nco = int(rng.integers(0, n_layers + 1))
+    return rng, shapes, H, d, n_layers, nco
+
+
 def test_random_stack_sweep():
-    """Seeded random layouts (up to 12 users; empty histories, users without candidates, single
-    candidates, prefix-only histories), H 1-4 and d 32-128 with H d a multiple of 128, 2-3 layers
-    of which 0 to all are
-    candidate-only.  Per batch: each layer's update against the oracle's layer on the GPU's
-    state before it, in relative Frobenius norm; the cached request equal to the full
-    request's candidates bit for bit; and a permutation of one user's candidates permuting
-    their outputs bit for bit.  (Every batch keeps at least one candidate.)"""
+    """Random layouts and stack shapes: each layer's update against the oracle's layer on the
+    GPU's state before it, in relative Frobenius norm; the cached request equal to the full
+    request's candidates bit for bit; a permutation of one user's candidates permuting their
+    outputs bit for bit."""
     for i in range(12):
-        rng = np.random.default_rng(7700 + i)
-        B = int(rng.integers(1, 13))
-        shapes = dict(prefix=rng.integers(0, 4, B), hist=rng.integers(0, 300, B) * (rng.random(B) > 0.15),
-                      cand=rng.integers(1, 40, B) * (rng.random(B) > 0.15))
-        if shapes["cand"].sum() == 0:
-            shapes["cand"][0] = 1
-        H, d = [(1, 128), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128)][int(rng.integers(0, 6))]   # D % 128 == 0
-        n_layers = int(rng.integers(2, 4))
-        nco = int(rng.integers(0, n_layers + 1))
+        rng, shapes, H, d, n_layers, nco = _random_stack_case(i)
+        B = len(shapes["cand"])
         what = f"stack sweep {i} (B={B} H={H} d={d} layers={n_layers} candidate-only={nco})"
         print(what, flush=True)
         x, off, cs, dl, ol = _setup(H, d, n_layers, seed=7800 + i, shapes=shapes)
@@ -451,3 +457,45 @@ def test_random_stack_sweep():
         cperm = np.arange(int(coff[-1]))
         cperm[coff[b]:coff[b + 1]] = coff[b] + (perm[cs[b]:off[b + 1]] - cs[b])
         assert torch.equal(xh2, xh) and torch.equal(xc2, xc[to_dev(cperm)]), f"{what}: candidate order"
+
+
+def test_random_user_token_sweep():
+    """The same random layouts with each user's prefix rows as its user tokens, updated in the
+    candidate-only layers (at least one such layer per case): per candidate-only layer the
+    update of the candidates and of the user tokens against the oracle's layer on the GPU's
+    own state, in relative Frobenius norm, and the other history rows frozen bit for bit;
+    then the cached request equal to the full request's candidates bit for bit."""
+    for i in range(12):
+        _, shapes, H, d, n_layers, nco = _random_stack_case(i)
+        nco = max(nco, 1)
+        p = np.asarray(shapes["prefix"])
+        what = f"user-token sweep {i} (B={len(p)} H={H} d={d} layers={n_layers} candidate-only={nco})"
+        print(what, flush=True)
+        x, off, cs, dl, ol = _setup(H, d, n_layers, seed=7900 + i, shapes=shapes)
+        hoff = np.concatenate([[0], np.cumsum(cs - off[:-1])])
+        coff = np.concatenate([[0], np.cumsum(off[1:] - cs)])
+        n_full = n_layers - nco
+        if n_full:
+            _, xc, xh, _ = _run(x, off, cs, dl[:n_full], 0, H, d)
+            prev_c, prev_h = _np(xc), _np(xh)
+        else:
+            prev_h, prev_c = RK.split_history_and_candidates(x.astype(np.float64), off, cs)[:2]
+        frozen_h = prev_h.copy()
+        is_p = np.zeros(len(prev_h), bool)
+        for b in range(len(p)):
+            is_p[hoff[b]:hoff[b] + p[b]] = True
+        for l in range(n_full + 1, n_layers + 1):
+            _, xc, xh, cache = _run(x, off, cs, dl[:l], l - n_full, H, d, user_tokens=p)
+            got_c, got_h = _np(xc), _np(xh)
+            assert np.array_equal(got_h[~is_p], frozen_h[~is_p]), f"{what}: a history row moved"
+            ref_p, ref_c, _, _ = RK.block_user_token_layer(prev_h[is_p], frozen_h, prev_c, ol[l - 1], p, hoff, coff,
+                                                           H, d, 10000.0, None)
+            _frob(got_c, ref_c, prev_c, f"{what}, candidates, layer {l}")
+            if is_p.any():
+                _frob(got_h[is_p], ref_p, prev_h[is_p], f"{what}, user tokens, layer {l}")
+            prev_c, prev_h = got_c, got_h
+        xc0 = RK.split_history_and_candidates(x, off, cs)[1]
+        again = rr().rr_ranker_cached_fwd(to_dev(xc0.astype(np.float32)), dl, cache, to_dev(hoff.astype(np.int32)),
+                                          to_dev(coff.astype(np.int32)), H, d)
+        torch.cuda.synchronize()
+        assert torch.equal(again, xc), f"{what}: cached request"
