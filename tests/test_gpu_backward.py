@@ -154,11 +154,11 @@ def _one_user(fb, b, h, dout):
     return BW.full_attention_backward(*args), BW.gradient_error_scale(*args)
 
 
-@pytest.mark.parametrize("cfg", [3, 6])
+@pytest.mark.parametrize("cfg", [3, 5, 6])
 def test_backward_full_size_sampled_users(cfg):
-    """The lognormal-history batch (d=64) and the padded skew batch (d=128) at full size; the
-    oracle checks whole users (every row, one head each): the shortest, median and longest
-    history."""
+    """The lognormal-history batch (d=64), the skew batch and the padded skew batch (d=128,
+    wide query tiles) at full size; the oracle checks whole users (every row, one head each):
+    the shortest, median and longest history."""
     fb = W.make_config(cfg)
     got = _train_step(fb, 7800 + cfg, host=False)
     _, _, dq, dk, dv = got["raw"]
