@@ -103,6 +103,26 @@ def test_rope_attention_config3_sampled():
     assert_close(got[rows, heads], ref, "bf16", "config 3 with rotary q/k, sampled")
 
 
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_rope_step_full_size_sampled(cfg):
+    """The rotary step in the form the benchmark times it -- keys rotated by rr_rope_qk, queries
+    inside rr_attn_fwd_rope -- on the short-history and skew batches at full size: every
+    output bit-identical to rotating q and k first and running rr_attn_fwd, and sampled rows
+    against the rotary oracle."""
+    fb = W.make_config(cfg)
+    dv = full_dev(fb)
+    _, k_rot = _rope_dev(None, dv["k"], dv["offsets"], dv["cand_start"])
+    q_rot, _ = _rope_dev(dv["q"], None, dv["offsets"], dv["cand_start"])
+    fused = rr().rr_attn_fwd_rope(dv["q"], k_rot, dv["v"], dv["offsets"], dv["cand_start"])
+    two_pass = rr().rr_attn_fwd(q_rot, k_rot, dv["v"], dv["offsets"], dv["cand_start"])
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two_pass), f"config {cfg}: in-kernel rotation differs from the rotary pass"
+    rows, heads = sample_full_rows(fb, 2, seed=cfg)
+    pos = R.right_anchored_positions(fb.offsets, fb.cand_start)
+    ref = A.full_attention_rows(R.rope(fb.q, pos), R.rope(fb.k, pos), fb.v, fb.offsets, fb.cand_start, rows, heads)
+    assert_close(_np(fused)[rows, heads], ref, "bf16", f"config {cfg} rotary step, sampled")
+
+
 def test_rope_candidates_interchangeable_bit_identical():
     rng = np.random.default_rng(31)
     fb = W.make_full_batch(rng, "rope-perm", prefix=[4, 2, 0, 3], hist=[700, 90, 0, 260],
