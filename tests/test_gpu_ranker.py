@@ -499,3 +499,47 @@ def test_random_user_token_sweep():
                                           to_dev(coff.astype(np.int32)), H, d)
         torch.cuda.synchronize()
         assert torch.equal(again, xc), f"{what}: cached request"
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_stack_full_size_sampled_users(cfg):
+    """The stack as the benchmark runs it (8 layers, the last 2 candidate-only, the benchmark's
+    random inputs of width D = H d) on the lognormal-history and skew batches at full size,
+    with its first l layers for l = 1..8: for sampled users (the shortest and median
+    histories, and on the lognormal batch the longest), each layer's update of that user's
+    rows against the oracle's layer on the GPU's state of those rows before it, in relative
+    Frobenius norm, and the frozen history unchanged through the candidate-only layers.
+    Users never read each other's rows, so the oracle runs each sampled user alone."""
+    fb = W.make_config(cfg)
+    H, d = fb.H, fb.d
+    n_layers, nco = 8, 2
+    n_full = n_layers - nco
+    x, layers = W.ranker_inputs(fb.seed + 99, fb.T, n_layers, H * d)
+    dl = [(to_dev(g), to_dev(wq, torch.bfloat16), to_dev(wo, torch.bfloat16)) for g, wq, wo in layers]
+    ol = [RK.Layer(g.astype(np.float64), wq.astype(np.float64), wo.astype(np.float64)) for g, wq, wo in layers]
+    off, cs = fb.offsets, fb.cand_start
+    hoff = np.concatenate([[0], np.cumsum(cs - off[:-1])])
+    coff = np.concatenate([[0], np.cumsum(off[1:] - cs)])
+    order = np.argsort(fb.hist, kind="stable")
+    picks = sorted({int(order[0]), int(order[len(order) // 2])} | ({int(order[-1])} if cfg == 3 else set()))
+    state = {b: x[off[b]:off[b + 1]].astype(np.float64) for b in picks}
+    hist, cand = {}, {}
+    for l in range(1, n_layers + 1):
+        xd, xc, xh, _ = _run(x, off, cs, dl[:l], max(0, l - n_full), H, d)
+        for b in picks:
+            lo, hi, c = int(off[b]), int(off[b + 1]), int(cs[b])
+            what = f"config {cfg} user {b} ({c - lo} history, {hi - c} candidates), layer {l}"
+            if l <= n_full:
+                got = _np(xd[lo:hi])
+                ref = RK.block_full(state[b], ol[l - 1], np.array([0, hi - lo]), np.array([c - lo]), H, d)
+                _frob(got, ref, state[b], what)
+                state[b] = got
+                hist[b], cand[b] = got[:c - lo], got[c - lo:]
+            else:
+                assert np.array_equal(_np(xh[hoff[b]:hoff[b + 1]]), hist[b]), f"{what}: the history moved"
+                hb, cb = np.array([0, c - lo]), np.array([0, hi - c])
+                kh, vh = RK.history_kv(hist[b], ol[l - 1], hb, H, d)
+                got = _np(xc[coff[b]:coff[b + 1]])
+                _frob(got, RK.block_cand_only(cand[b], kh, vh, ol[l - 1], hb, cb, H, d), cand[b], what)
+                cand[b] = got
+        del xd, xc, xh
