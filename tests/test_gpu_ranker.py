@@ -543,3 +543,43 @@ def test_stack_full_size_sampled_users(cfg):
                 _frob(got, RK.block_cand_only(cand[b], kh, vh, ol[l - 1], hb, cb, H, d), cand[b], what)
                 cand[b] = got
         del xd, xc, xh
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_user_token_stack_full_size_sampled_users(cfg):
+    """The benchmarked stack with each user's prefix rows as its user tokens, on the
+    lognormal-history and skew batches at full size: after the full layers (checked in the
+    test above), each candidate-only layer's update of a sampled user's candidates and user
+    tokens against the oracle's layer on the GPU's own state of that user's rows, in
+    relative Frobenius norm, and the user's other history rows frozen bit for bit."""
+    fb = W.make_config(cfg)
+    H, d = fb.H, fb.d
+    n_layers, nco = 8, 2
+    n_full = n_layers - nco
+    x, layers = W.ranker_inputs(fb.seed + 99, fb.T, n_layers, H * d)
+    dl = [(to_dev(g), to_dev(wq, torch.bfloat16), to_dev(wo, torch.bfloat16)) for g, wq, wo in layers]
+    ol = [RK.Layer(g.astype(np.float64), wq.astype(np.float64), wo.astype(np.float64)) for g, wq, wo in layers]
+    off, cs, p = fb.offsets, fb.cand_start, np.asarray(fb.prefix)
+    hoff = np.concatenate([[0], np.cumsum(cs - off[:-1])])
+    coff = np.concatenate([[0], np.cumsum(off[1:] - cs)])
+    order = np.argsort(fb.hist, kind="stable")
+    picks = sorted({int(order[0]), int(order[len(order) // 2])} | ({int(order[-1])} if cfg == 3 else set()))
+    _, xc, xh, _ = _run(x, off, cs, dl[:n_full], 0, H, d)
+    hist = {b: _np(xh[hoff[b]:hoff[b + 1]]) for b in picks}
+    cand = {b: _np(xc[coff[b]:coff[b + 1]]) for b in picks}
+    frozen = {b: hist[b].copy() for b in picks}
+    del xc, xh
+    for l in range(n_full + 1, n_layers + 1):
+        _, xc, xh, _ = _run(x, off, cs, dl[:l], l - n_full, H, d, user_tokens=p)
+        for b in picks:
+            nh, nc, pb = int(cs[b] - off[b]), int(off[b + 1] - cs[b]), int(p[b])
+            what = f"config {cfg} user {b} ({pb} user tokens, {nh} history, {nc} candidates), layer {l}"
+            got_h, got_c = _np(xh[hoff[b]:hoff[b + 1]]), _np(xc[coff[b]:coff[b + 1]])
+            assert np.array_equal(got_h[pb:], frozen[b][pb:]), f"{what}: a history row moved"
+            ref_p, ref_c, _, _ = RK.block_user_token_layer(hist[b][:pb], frozen[b], cand[b], ol[l - 1], np.array([pb]),
+                                                           np.array([0, nh]), np.array([0, nc]), H, d, 10000.0, None)
+            _frob(got_c, ref_c, cand[b], f"{what}, candidates")
+            if pb:
+                _frob(got_h[:pb], ref_p, hist[b][:pb], f"{what}, user tokens")
+            hist[b], cand[b] = got_h, got_c
+        del xc, xh
