@@ -398,6 +398,9 @@ def test_user_token_cached_request_bit_identical():
     assert torch.equal(again, xc)
 
 
+N_STACK_CASES = 12
+
+
 def _random_stack_case(i):
     """Layout and stack shape of random case i: up to 12 users (empty histories, users without
     candidates, single candidates, prefix-only histories; at least one candidate), H and d
@@ -419,7 +422,7 @@ def test_random_stack_sweep():
     GPU's state before it, in relative Frobenius norm; the cached request equal to the full
     request's candidates bit for bit; a permutation of one user's candidates permuting their
     outputs bit for bit."""
-    for i in range(12):
+    for i in range(N_STACK_CASES):
         rng, shapes, H, d, n_layers, nco = _random_stack_case(i)
         B = len(shapes["cand"])
         what = f"stack sweep {i} (B={B} H={H} d={d} layers={n_layers} candidate-only={nco})"
@@ -465,7 +468,7 @@ def test_random_user_token_sweep():
     update of the candidates and of the user tokens against the oracle's layer on the GPU's
     own state, in relative Frobenius norm, and the other history rows frozen bit for bit;
     then the cached request equal to the full request's candidates bit for bit."""
-    for i in range(12):
+    for i in range(N_STACK_CASES):
         _, shapes, H, d, n_layers, nco = _random_stack_case(i)
         nco = max(nco, 1)
         p = np.asarray(shapes["prefix"])
